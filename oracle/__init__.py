@@ -1,0 +1,35 @@
+"""Float64 CPU oracle for paged GQA decode attention — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, calls or links anything here, and this
+package never imports the product path.  It is plain, slow and meant to be
+checked by eye against the pages it cites:
+
+* ``attention.paged_decode_attention`` — the definition of single-token decode
+  attention over a paged KV cache, written out in float64.
+* ``cache.kv_append`` / ``cache.gather_sequence`` — the block-table scatter and
+  gather, as integer indexing.
+* ``fp8.decode_e4m3fn`` — OCP FP8 E4M3 (finite-only, max 448) decoding from the
+  format definition.
+* ``online.chunked_attention`` / ``online.merge_partials`` — the online-softmax
+  block update and the log-sum-exp merge of partial results, in the pages' own
+  steps, to pin the split decomposition against the direct form.
+* ``formulas`` — KV-cache byte count and decode-attention arithmetic intensity.
+
+Every function is pinned by ``-m "not gpu"`` tests to something other than
+itself (brute force, a float64 library routine, closed forms, invariants and
+values printed on the pages).  No function here is "parity unpinned".
+"""
+from .attention import paged_decode_attention, dense_decode_attention
+from .cache import kv_append, gather_sequence
+from .fp8 import decode_e4m3fn
+from .bf16 import bf16_to_float64
+from .online import chunked_attention, merge_partials
+from .formulas import kv_cache_bytes, decode_attention_flops, decode_attention_intensity
+
+__all__ = [
+    "paged_decode_attention", "dense_decode_attention", "kv_append", "gather_sequence",
+    "decode_e4m3fn", "bf16_to_float64", "chunked_attention", "merge_partials",
+    "kv_cache_bytes", "decode_attention_flops", "decode_attention_intensity",
+]

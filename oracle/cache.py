@@ -1,0 +1,57 @@
+"""Paged KV cache: block-table gather and single-token append (oracle side).
+
+Cites:
+* *Module 10: Inference and Deployment Serving* (wrwei.github.io), "Mapping
+  logical positions to physical blocks": the cache is cut into fixed-size
+  blocks in one shared pool; a per-sequence block table maps logical block i
+  to a physical block; a sequence's blocks need not be adjacent; with 16-token
+  blocks at most 15 tail slots are wasted.
+* *Ch. 6 Inference Efficiency and Model Serving* (Stochastic Parrot vol. 1),
+  §6.4: logical positions split into fixed blocks, mapped to non-contiguous
+  physical blocks; the last block has at most one block of internal waste.
+* *LLM Inference Systems Engineering* (jasonzhang109), §2.1.3: the cache only
+  holds positions already forwarded; each step first commits the pending
+  token's K/V, then attends.
+* *The Mathematics of Transformer Inference* (hs-black), §1: decode reads the
+  cache for attention and appends the new token's own K and V.
+
+Pool layout (a reading; the pages fix no layout): ``pool[num_blocks][H_kv][BS][d_h]``;
+token t of sequence b lives in physical block ``block_table[b][t // BS]`` at
+slot ``t % BS``.
+"""
+import numpy as np
+
+
+def gather_sequence(pool: np.ndarray, block_table_row: np.ndarray, ctx: int,
+                    block_size: int) -> np.ndarray:
+    """Return the sequence's cached rows in logical order: ``[H_kv][ctx][d_h]``.
+
+    Only the first ceil(ctx / BS) table entries are read, and only the first
+    ``ctx`` slots of the logical stream are returned.
+    """
+    ctx = int(ctx)
+    t = np.arange(ctx)
+    phys = np.asarray(block_table_row)[t // block_size]
+    slot = t % block_size
+    rows = pool[phys, :, slot, :]            # [ctx][H_kv][d_h]
+    return np.ascontiguousarray(np.transpose(rows, (1, 0, 2)))
+
+
+def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+              block_tables: np.ndarray, positions: np.ndarray, block_size: int):
+    """Write token ``positions[b]`` of every sequence b into the pools.
+
+    ``k_new/v_new`` are ``[B][H_kv][d_h]``.  A negative position means "no
+    append for this sequence".  Returns new pools; inputs are not modified.
+    Only the one slot per (sequence, KV head) changes.
+    """
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    for b, pos in enumerate(np.asarray(positions)):
+        pos = int(pos)
+        if pos < 0:
+            continue
+        blk = int(block_tables[b][pos // block_size])
+        slot = pos % block_size
+        k_out[blk, :, slot, :] = k_new[b]
+        v_out[blk, :, slot, :] = v_new[b]
+    return k_out, v_out
