@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: KV-read GB/s (vs MI355X peak HBM bandwidth) and us/step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+One step = one pass of the decode hot path over one batch: the KV append of the
+new token (for workloads that append) followed by paged decode attention
+(split pass + log-sum-exp merge), all through the C ABI.  Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.  To measure HBM
+rather than the 256 MB on-die Infinity Cache, consecutive steps rotate over
+enough copies of the KV pool that each step's KV bytes were last touched at
+least 1 GiB of other KV reads ago.
+
+Prints one JSON line (rank 0, N=1).  `value` = algorithmic KV bytes per step /
+step time.  `roofline.achieved` = the same bytes / the decode-attention call's
+average duration measured with HIP events on the launch stream.  The float64
+CPU oracle is timed on a bounded sample as `cpu_baseline`.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+ROTATE_BYTES = 1 << 30         # distance between reuses of one pool copy
+METRIC = "decode-attention KV-read HBM GB/s (% of MI355X peak) and µs/step"
+
+
+def kv_bytes_per_step(spec, context_lens):
+    """Algorithmic bytes: every attended K and V element at stored width, plus fp8 scales."""
+    import numpy as np
+    esz = 1 if spec.kv_dtype == "fp8" else 2
+    ctx = context_lens.astype(np.int64)
+    total = int(ctx.sum()) * spec.num_kv_heads * spec.head_dim * 2 * esz
+    if spec.kv_dtype == "fp8":
+        nb = (ctx + spec.block_size - 1) // spec.block_size
+        total += int(nb.sum()) * spec.num_kv_heads * 2 * 4
+    return total
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gqa_decode_attention_paged_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(workload):
+    """HBM bytes per decode call from committed rocprofv3 PMC runs, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(case, kv_bytes, min_seconds):
+    """Time the float64 oracle (as it stands) on whole steps of the workload, 1 BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    spec = case["spec"]
+    n, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            oracle.paged_decode_attention(case["q"], case["k_pool_full"], case["v_pool_full"],
+                                          case["block_tables"], case["context_lens"],
+                                          spec.block_size, case["softmax_scale"], spec.kv_dtype,
+                                          case["k_scale"], case["v_scale"])
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                break
+    per_step = el / n
+    return {"value": round(kv_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} whole step(s) of the {spec.name} workload, float64 numpy oracle, "
+                      f"1 BLAS thread, {el:.1f} s total ({per_step * 1e3:.1f} ms/step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["tiny", "llama8b", "batched", "long", "mha_fp8"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps eagerly instead of replaying a HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device copies (for scaling PMC byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this decode-attention path has no "
+              "multi-GPU mode (see the sharding notes in the design document).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gqa_decode_attention_paged_amd as gqa
+    from workloads import make_case, SPECS
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 256 << 20, "copies": 5}))
+        return
+
+    gqa.load()
+    dev = torch.device("cuda:0")
+    spec = SPECS[args.workload]
+    case = make_case(spec, seed=args.seed)
+    kv_bytes = kv_bytes_per_step(spec, case["context_lens"])
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def pool(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev) if a.dtype == np.uint8 else bf16(a)
+
+    q = bf16(case["q"])
+    bt = torch.from_numpy(case["block_tables"]).to(dev)
+    ctx = torch.from_numpy(case["context_lens"]).to(dev)
+    pos = torch.from_numpy(case["positions"]).to(dev)
+    k_new = bf16(case["k_new"]) if case["k_new"] is not None else None
+    v_new = bf16(case["v_new"]) if case["v_new"] is not None else None
+    ks = torch.from_numpy(case["k_scale"]).to(dev) if case["k_scale"] is not None else None
+    vs = torch.from_numpy(case["v_scale"]).to(dev) if case["v_scale"] is not None else None
+    k0, v0 = pool(case["k_pool"]), pool(case["v_pool"])
+    copies = min(256, max(1, math.ceil(ROTATE_BYTES / kv_bytes) + 1))
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    max_ctx = int(case["context_lens"].max())
+    shape = gqa.make_shape(spec.num_seqs, spec.num_q_heads, k0, bt)
+    ws = gqa.make_workspace(shape, max_ctx, dev)
+    out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((spec.num_seqs, spec.num_q_heads), dtype=torch.float32, device=dev)
+    scale = case["softmax_scale"]
+
+    def step(i):
+        kc, vc = pools[i % copies]
+        if k_new is not None:      # fused: commit the new token and attend, one kernel
+            gqa.paged_decode_append_attention(q, k_new, v_new, pos, kc, vc, bt, ctx, max_ctx,
+                                              scale, out=out, out_lse=lse, workspace=ws)
+        else:
+            gqa.paged_decode_attention(q, kc, vc, bt, ctx, max_ctx, scale, ks, vs, out=out,
+                                       out_lse=lse, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    graph = None
+    if not args.no_graph:
+        # The K timed steps are recorded once into a HIP graph and replayed, so the
+        # GPU runs them back to back without Python launch gaps.  Every step still
+        # launches the full decode kernel on its own pool copy.
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        torch.cuda.synchronize()
+        graph.replay()                      # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(stop)
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = gpu_ms / args.steps
+    achieved = kv_bytes / (call_ms * 1e-3) / 1e9
+    kernel = ("paged_decode_kernel (fused KV append + split attention + log-sum-exp merge)"
+              if k_new is not None else "paged_decode_kernel (split attention + log-sum-exp merge)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.kv_dtype == "bf16" else "fp8",
+        "data": "synthetic (seeded N(0,1) q/k/v, random block placement; no weights)",
+        "config": {
+            "workload": spec.name, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+            "block_size": spec.block_size, "kv_dtype": spec.kv_dtype,
+            "context_lens_total": int(case["context_lens"].sum()), "append": spec.append,
+            "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": counted_traffic(spec.name),
+            "kernel": kernel,
+            "kernel_us_events": round(call_ms * 1e3, 3),
+            "timing": ("HIP events on the launch stream around one replay of a graph of the "
+                       "K steps (one kernel per step), divided by K" if graph is not None else
+                       "HIP events around K eager steps, divided by K"),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, kv_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

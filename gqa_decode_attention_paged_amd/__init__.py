@@ -1,0 +1,216 @@
+"""Python binding of the paged GQA decode-attention library (libgqa_paged.so).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI declared in ``include/gqa_paged.h``.  PyTorch supplies
+device memory and the stream; there is no CPU fallback — if the shared library
+is missing, ``load()`` raises.
+
+Tensor conventions (all on the same CUDA/HIP device):
+  q             [B][H_q][d_h]    torch.bfloat16
+  k_cache/v_cache [num_blocks][H_kv][block_size][d_h]  torch.bfloat16, or
+                torch.uint8 / torch.float8_e4m3fn holding OCP E4M3 codes
+  k_scale/v_scale [num_blocks][H_kv] torch.float32 (fp8 pools only)
+  block_tables  [B][max_blocks_per_seq] torch.int32
+  context_lens, positions [B] torch.int32
+  out           [B][H_q][d_h] torch.float32; out_lse [B][H_q] torch.float32
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "load", "GqaError", "PagedShape", "kv_append", "paged_decode_attention",
+    "workspace_size", "num_splits", "kv_gather", "last_error", "version", "LIB_PATH",
+    "paged_decode_append_attention", "make_workspace", "workspace_init", "make_shape",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_paged.so")
+
+GQA_KV_BF16 = 0
+GQA_KV_FP8_E4M3 = 1
+STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
+                3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
+
+
+class PagedShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def load():
+    """Load libgqa_paged.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gqa_decode_attention_paged_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    S = ctypes.POINTER(PagedShape)
+    lib.gqa_kv_append.argtypes = [S, _P, _P, _P, _P, _P, _P, _P]
+    lib.gqa_kv_append.restype = ctypes.c_int
+    lib.gqa_decode_num_splits.argtypes = [ctypes.c_int32]
+    lib.gqa_decode_num_splits.restype = ctypes.c_int32
+    lib.gqa_paged_decode_workspace_size.argtypes = [S, ctypes.c_int32]
+    lib.gqa_paged_decode_workspace_size.restype = ctypes.c_size_t
+    lib.gqa_paged_decode_attention.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                               ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gqa_paged_decode_attention.restype = ctypes.c_int
+    lib.gqa_paged_decode_append_attention.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                      ctypes.c_int32, ctypes.c_float, _P, _P,
+                                                      _P, ctypes.c_size_t, _P]
+    lib.gqa_paged_decode_append_attention.restype = ctypes.c_int
+    lib.gqa_paged_decode_workspace_init.argtypes = [S, ctypes.c_int32, _P, ctypes.c_size_t, _P]
+    lib.gqa_paged_decode_workspace_init.restype = ctypes.c_int
+    lib.gqa_kv_gather.argtypes = [S, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.gqa_kv_gather.restype = ctypes.c_int
+    lib.gqa_last_error.argtypes = []
+    lib.gqa_last_error.restype = ctypes.c_char_p
+    lib.gqa_version.argtypes = []
+    lib.gqa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().gqa_last_error().decode()
+
+
+def version() -> str:
+    return load().gqa_version().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise GqaError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _kv_dtype(cache) -> int:
+    import torch
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return GQA_KV_FP8_E4M3
+    if cache.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return GQA_KV_BF16
+    raise TypeError(f"unsupported KV cache dtype {cache.dtype}")
+
+
+def make_shape(num_seqs, num_q_heads, k_cache, block_tables) -> PagedShape:
+    nb, hkv, bs, d = k_cache.shape
+    return PagedShape(num_seqs, num_q_heads, hkv, d, bs, nb, block_tables.shape[1],
+                      _kv_dtype(k_cache))
+
+
+def num_splits(context_len: int) -> int:
+    """Partial attentions a sequence of this length is split into (host policy)."""
+    return int(load().gqa_decode_num_splits(int(context_len)))
+
+
+def workspace_size(shape: PagedShape, max_context_len: int) -> int:
+    return int(load().gqa_paged_decode_workspace_size(ctypes.byref(shape), int(max_context_len)))
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions):
+    """Write one new token per sequence into the paged pools (in place)."""
+    lib = load()
+    shape = make_shape(k_new.shape[0], k_cache.shape[1], k_cache, block_tables)
+    _check(lib.gqa_kv_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                             _ptr(v_cache), _ptr(block_tables), _ptr(positions),
+                             _stream(k_cache)))
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                           softmax_scale=None, k_scale=None, v_scale=None, out=None,
+                           out_lse=None, workspace=None, return_lse=True):
+    """Decode attention for a batch; returns (out, lse) (lse None if not requested)."""
+    import torch
+    lib = load()
+    B, Hq, D = q.shape
+    shape = make_shape(B, Hq, k_cache, block_tables)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(shape, max_context_len, q.device)
+    _check(lib.gqa_paged_decode_attention(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, out_lse
+
+
+def make_workspace(shape: PagedShape, max_context_len: int, device):
+    """A zero-filled workspace (its split arrival counters must start at zero)."""
+    import torch
+    nbytes = workspace_size(shape, max_context_len)
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, block_tables,
+                                  context_lens, max_context_len, softmax_scale=None, out=None,
+                                  out_lse=None, workspace=None, return_lse=True):
+    """Fused decode step: commit the new token at positions[b], then attend (one kernel)."""
+    import torch
+    lib = load()
+    B, Hq, D = q.shape
+    shape = make_shape(B, Hq, k_cache, block_tables)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(shape, max_context_len, q.device)
+    _check(lib.gqa_paged_decode_append_attention(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, out_lse
+
+
+def workspace_init(shape: PagedShape, max_context_len: int, workspace):
+    """Zero a workspace's arrival counters on the current stream."""
+    _check(load().gqa_paged_decode_workspace_init(
+        ctypes.byref(shape), int(max_context_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(workspace)))
+
+
+def kv_gather(cache, block_tables, seq, num_tokens):
+    """Copy sequence ``seq``'s first ``num_tokens`` rows out of a pool: [H_kv][T][d_h]."""
+    import torch
+    lib = load()
+    nb, hkv, bs, d = cache.shape
+    shape = PagedShape(block_tables.shape[0], hkv, hkv, d, bs, nb, block_tables.shape[1],
+                       _kv_dtype(cache))
+    out = torch.empty((hkv, num_tokens, d), dtype=cache.dtype, device=cache.device)
+    _check(lib.gqa_kv_gather(ctypes.byref(shape), _ptr(cache), _ptr(block_tables), int(seq),
+                             int(num_tokens), _ptr(out), _stream(cache)))
+    return out

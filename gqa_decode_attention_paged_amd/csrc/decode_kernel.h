@@ -1,0 +1,571 @@
+// Paged GQA decode attention: one fused kernel per decode step.
+//
+// Workgroup (split, KV head, sequence) computes, for the G query heads sharing
+// the KV head, attention over one contiguous token range of the sequence (its
+// "split"), then merges with the other splits of the same (sequence, KV head):
+// every workgroup publishes its partial result, and the last one to arrive
+// (atomic counter) combines them by log-sum-exp.  Optionally the kernel also
+// commits the step's new token into the cache (fused KV append).
+//
+// Method (cites):
+//  * scores s_t = scale <q, k_t>, softmax over t, weighted sum of v_t; query
+//    head h reads KV head h / G — *The Mathematics of Transformer Inference*
+//    (hs-black) §1, §4, §5; *Module 10: Inference and Deployment Serving*
+//    (wrwei.github.io), Lab 2 (each KV head repeated over consecutive heads).
+//  * K/V rows come through the block table, valid tokens only — *Module 10*,
+//    "Mapping logical positions to physical blocks"; *The Mathematics of
+//    Transformer Inference* §9.
+//  * per-chunk running max, exponential sum and unnormalised output — the
+//    online-softmax update of *LLM Inference Systems Engineering*
+//    (jasonzhang109) §2.8.3; splits merged by log-sum-exp as for sequence-
+//    sharded KV, *The Mathematics of Transformer Inference* §8.
+//  * the step commits the new token, then its query attends over the cache
+//    including it — *LLM Inference Systems Engineering* §2.1.3.
+//  * fp8 K/V dequantised in-kernel with a per-(block, head) scale — *The
+//    Mathematics of Transformer Inference* §11.
+//
+// gfx950 mapping.  A (block, KV head) tile is BS contiguous rows of D elements.
+// LPT = D/8 lanes cover one token row, 8 elements each (16 B bf16 / 8 B fp8), so
+// one wave load instruction reads TPI = 64/LPT whole rows, fully coalesced.
+// q for the G heads stays in registers (this lane's 8 dims).  A row's partial
+// dot products are summed across its lanes with DPP (xor 1, xor 2, half-row
+// mirror, row mirror), which leaves identical bits in every lane of the row.
+// Each of the TPI rows is its own online-softmax stream (tokens r, r+TPI, ...);
+// streams merge across the wave at the end, then across waves through LDS.
+// A wave walks its chunks (CT tokens) with the next chunk's loads in flight
+// while the current one is computed; the chunk's block ids come from one
+// vector load per wave, read out with readlane.
+//
+// The running max moves lazily: only when a chunk's max exceeds the reference
+// by more than 2^kLazyLog2 in weight, so weights stay <= 256; o/l and m + log2 l
+// are exact for any reference, so this only skips rescales.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace gqa {
+
+struct DecodeParams {
+  const uint16_t* q;            // [B][Hq][D] bf16
+  void* k_cache;                // [NB][Hkv][BS][D]; written only by the fused append
+  void* v_cache;
+  const float* k_scale;         // [NB][Hkv] (fp8 only)
+  const float* v_scale;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* context_lens;  // [B]
+  const uint16_t* k_new;        // [B][Hkv][D] fused append, or null
+  const uint16_t* v_new;
+  const int32_t* positions;     // [B] slot of the appended token, or null
+  float* out;                   // [B][Hq][D]
+  float* out_lse;               // [B][Hq] or null
+  float* ws_o;                  // [B][Hkv][max_splits][G][D] partial outputs (normalised)
+  float* ws_lse;                // [B][Hkv][max_splits][G]    partial base-2 lse
+  uint32_t* counters;           // [B][Hkv] arrivals; zero between calls
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_splits;
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+constexpr float kLazyLog2 = 8.0f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LPT lanes of a token row (LPT = 8 or 16); same bits in every lane.
+template <int LPT>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0xB1>(x);        // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);        // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);       // row_half_mirror
+  if constexpr (LPT == 16) x += dpp<0x140>(x);   // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+// Cross-workgroup publication of split partials without flushing L2.  Partial
+// results are written and read with agent-scope coherent accesses (the sc1
+// cache policy: relaxed agent-scope atomic stores/loads, and 128-bit buffer
+// loads carrying the same policy), so no L2 writeback or invalidate is needed;
+// the writer waits for its stores to complete before the arrival counter is
+// bumped, and the reader only loads after it has seen the last arrival.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every vector memory access of this wave (stores included) done.
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicySc1 = 16;         // buffer instruction cache-policy bit "sc1"
+constexpr int kBufferRsrcWord3 = 0x00020000;  // raw 32-bit buffer resource (gfx9 family)
+
+template <bool FP8>
+struct KVTraits {
+  using Vec = uint4;                 // 8 bf16
+  static constexpr int kBytes = 2;
+};
+template <>
+struct KVTraits<true> {
+  using Vec = uint2;                 // 8 fp8 codes
+  static constexpr int kBytes = 1;
+};
+
+template <bool FP8>
+__device__ __forceinline__ void widen8(const typename KVTraits<FP8>::Vec& v, float* f) {
+  if constexpr (FP8) {
+    fp8x4_to_f32(v.x, f);
+    fp8x4_to_f32(v.y, f + 4);
+  } else {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  }
+}
+
+// Copy the appended token's K and V rows of (b, kvh) into the cache (bf16 pools).
+__device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kvh, int pos, int D,
+                                            int BS) {
+  const int units = D / 8;
+  if ((int)threadIdx.x >= units || pos < 0 || pos >= p.max_blocks * BS) return;
+  const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / BS];
+  if (blk < 0 || blk >= p.num_blocks) return;
+  const size_t src = ((size_t)b * p.num_kv_heads + kvh) * D + threadIdx.x * 8;
+  const size_t dst = (((size_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * D + threadIdx.x * 8;
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + dst) =
+      *reinterpret_cast<const uint4*>(p.k_new + src);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + dst) =
+      *reinterpret_cast<const uint4*>(p.v_new + src);
+}
+
+template <int D, int BS, int G, bool FP8, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParams p) {
+  constexpr int LPT = D / 8;                 // lanes per token row
+  constexpr int TPI = kWave / LPT;           // rows per load instruction
+  constexpr int CT = G >= 8 ? 16 : 32;       // tokens per wave chunk
+  constexpr int NI = CT / TPI;               // load instructions per chunk (each of K, V)
+  constexpr int EPC = CT >= BS ? CT / BS : 1;  // block-table entries per chunk
+  constexpr int CPG = kWave / EPC;           // chunks per preloaded table group
+  constexpr int ESZ = KVTraits<FP8>::kBytes;
+  constexpr int NT = WAVES * kWave;
+  static_assert(BS % TPI == 0 && kChunkTokens % CT == 0, "tile geometry");
+  using Vec = typename KVTraits<FP8>::Vec;
+
+  // Workgroup -> (split, KV head, sequence).  When the number of (sequence,
+  // KV head) pairs is a multiple of 8, all splits of one pair are placed on
+  // one XCD (workgroups are dealt to the 8 XCDs round robin), so the partial
+  // results the last workgroup merges stay in that XCD's L2.
+  const int S = gridDim.x;
+  const int P = gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + S * (blockIdx.y + gridDim.y * blockIdx.z);
+  int split, pair;
+  if ((P & 7) == 0) {
+    const int xcd = lin & 7, slot = lin >> 3;
+    pair = (slot / S) * 8 + xcd;
+    split = slot % S;
+  } else {
+    pair = lin / S;
+    split = lin % S;
+  }
+  const int kvh = pair % p.num_kv_heads;
+  const int b = pair / p.num_kv_heads;
+  const int h0 = kvh * G;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int row = lane / LPT;
+  const int col = lane % LPT;
+
+  // LDS: per-wave partial sums during the split merge, then (reused) the split
+  // weights and float4 partial sums of the final merge.
+  constexpr int C4 = G * D / 4;                    // float4 columns of one head group
+  constexpr int SP = NT >= C4 ? NT / C4 : 1;       // threads per column in the final merge
+  constexpr int kAccFloats = WAVES * G * D;
+  constexpr int kMergeFloats = G * kWave + 4 * ((G + 3) / 4) + 4 * SP * C4;
+  constexpr int kBufFloats = kAccFloats > kMergeFloats ? kAccFloats : kMergeFloats;
+  __shared__ __attribute__((aligned(16))) float sm_buf[kBufFloats];
+  __shared__ float sm_m[WAVES][G];
+  __shared__ float sm_l[WAVES][G];
+  __shared__ int sm_flag[WAVES + 1];
+  auto sm_acc = [&](int w, int g, int d) -> float& { return sm_buf[(w * G + g) * D + d]; };
+
+  const int ctx = p.context_lens[b];
+  const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS;
+  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx);
+  const bool too_long = plan.num_splits > p.max_splits;
+  const int pos = p.positions ? p.positions[b] : -1;
+  const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
+  const int owner = (!degenerate && pos >= 0 && pos < ctx) ? pos / plan.split_tokens : 0;
+  if (p.positions && split == owner) append_rows(p, b, kvh, pos, D, BS);
+
+  if (degenerate) {
+    if (split != 0) return;
+    const bool bad = ctx_bad || too_long;
+    const float v = bad ? __builtin_nanf("") : 0.f;
+    for (int i = tid; i < G * D; i += NT)
+      p.out[((size_t)b * p.num_q_heads + h0) * D + i] = v;
+    if (p.out_lse && tid < G)
+      p.out_lse[(size_t)b * p.num_q_heads + h0 + tid] = bad ? __builtin_nanf("") : kNegInf;
+    return;
+  }
+  const int nsplit = plan.num_splits;
+  if (split >= nsplit) return;
+  const int s0 = split * plan.split_tokens;
+  const int s1 = min(ctx, s0 + plan.split_tokens);
+  const int app = (pos >= s0 && pos < s1) ? pos : -1;     // appended token read from k_new
+
+  // q: this lane's 8 dims of each of the G heads.
+  const uint16_t* qp = p.q + ((size_t)b * p.num_q_heads + h0) * D + col * 8;
+  uint32_t qw[G][4];
+  float qf[FP8 ? G : 1][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint4 v = *reinterpret_cast<const uint4*>(qp + (size_t)g * D);
+    qw[g][0] = v.x; qw[g][1] = v.y; qw[g][2] = v.z; qw[g][3] = v.w;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qf[g][2 * j] = bf16_lo(qw[g][j]);
+        qf[g][2 * j + 1] = bf16_hi(qw[g][j]);
+      }
+    }
+  }
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
+  }
+  bool bad = false;
+
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks;
+  const char* kbase = static_cast<const char*>(p.k_cache);
+  const char* vbase = static_cast<const char*>(p.v_cache);
+  constexpr size_t kTileBytes = (size_t)BS * D * ESZ;
+  const size_t block_stride = (size_t)p.num_kv_heads * kTileBytes;
+  const size_t new_off = ((size_t)b * p.num_kv_heads + kvh) * D * 2 + (size_t)col * 16;
+
+  const int nchunks = (s1 - s0 + CT - 1) / CT;
+  const int my_n = wave < nchunks ? (nchunks - wave + WAVES - 1) / WAVES : 0;
+
+  // Block ids of this wave's chunks j0 .. j0+CPG-1: lane = (j - j0) * EPC + e.
+  int j0 = 0;
+  auto load_ids = [&](int jbase) {
+    const int jj = jbase + lane / EPC;
+    const int tok = s0 + (wave + jj * WAVES) * CT + (lane % EPC) * BS;
+    return (jj < my_n && tok < s1) ? bt[tok / BS] : 0;
+  };
+  int ids = load_ids(0);
+
+  // Instruction i of chunk j reads TPI rows of one (block, KV head) tile: a
+  // wave-uniform tile base (block id via readlane) plus this lane's 16 B slot.
+  const uint32_t lane_off = (uint32_t)lane * 8 * ESZ;
+  auto tile_base = [&](int j, int i, const char* pool, bool track) -> const char* {
+    const int e = CT >= BS ? (i * TPI) / BS : 0;
+    int phys = __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e);
+    const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
+    if (track) bad |= !ok;
+    phys = ok ? phys : 0;
+    const int first = (s0 + (wave + j * WAVES) * CT + i * TPI) % BS;   // uniform
+    return pool + (size_t)phys * block_stride + (size_t)kvh * kTileBytes +
+           (size_t)first * D * ESZ;
+  };
+  auto chunk_start = [&](int j) { return s0 + (wave + j * WAVES) * CT; };
+
+  // Issue the loads of one tile (K or V) of chunk j.  Branch-free: every row
+  // reads an in-bounds slot (rows past the split end read their block's unused
+  // slots, whole groups past it read block 0) and compute masks them.  If the
+  // chunk holds the appended token, its row is also loaded from the new-token
+  // buffer into `nr`, and compute swaps it in.
+  auto issue = [&](int j, const char* pool, const char* nbase, Vec (&r)[NI], Vec& nr,
+                   float (&sc)[NI], const float* scales, bool track) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      r[i] = *reinterpret_cast<const Vec*>(tile_base(j, i, pool, track) + lane_off);
+      if constexpr (FP8) {
+        const int e = CT >= BS ? (i * TPI) / BS : 0;
+        int phys = __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e);
+        phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;
+        sc[i] = scales[(size_t)phys * p.num_kv_heads + kvh];
+      }
+    }
+    if constexpr (!FP8) {
+      const int t0 = chunk_start(j);
+      if (app >= t0 && app < t0 + CT) nr = *reinterpret_cast<const Vec*>(nbase + new_off);
+    }
+  };
+
+  Vec kr[NI], vr[NI], kn, vn;
+  float ks[NI], vs[NI];
+  float s[NI][G];
+  const char* knew = reinterpret_cast<const char*>(p.k_new);
+  const char* vnew = reinterpret_cast<const char*>(p.v_new);
+
+  // Rotating pipeline: K(j+1) is issued right after the scores of chunk j, V(j+1)
+  // right after its value sums, so the next chunk's loads fly during compute with
+  // no extra registers.
+  if (my_n > 0) {
+    issue(0, kbase, knew, kr, kn, ks, p.k_scale, true);
+    issue(0, vbase, vnew, vr, vn, vs, p.v_scale, false);
+  }
+  for (int j = 0; j < my_n; ++j) {
+    const int t0 = chunk_start(j);
+    const bool masked = t0 + CT > s1;
+    const bool has_app = app >= t0 && app < t0 + CT;           // uniform
+    const int i_app = (app - t0) / TPI;
+    const bool row_app = has_app && (app - t0) % TPI == row;
+    // scores (base-2 units)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      Vec kk = kr[i];
+      if (has_app && i == i_app && row_app) kk = kn;
+      float part[G];
+      if constexpr (FP8) {
+        float kf[8];
+        widen8<true>(kk, kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) a = fmaf(qf[g][k], kf[k], a);
+          part[g] = a;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a = dot2_bf16(qw[g][0], kk.x, 0.f);
+          a = dot2_bf16(qw[g][1], kk.y, a);
+          a = dot2_bf16(qw[g][2], kk.z, a);
+          part[g] = dot2_bf16(qw[g][3], kk.w, a);
+        }
+      }
+      const float sc = FP8 ? p.scale_log2 * ks[i] : p.scale_log2;
+      const bool valid = !masked || (t0 + i * TPI + row < s1);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float tot = row_sum<LPT>(part[g]) * sc;
+        s[i][g] = valid ? tot : kNegInf;
+      }
+    }
+    if (j + 1 < my_n) {
+      if (j + 1 - j0 >= CPG) {
+        j0 += CPG;
+        ids = load_ids(j0);
+      }
+      issue(j + 1, kbase, knew, kr, kn, ks, p.k_scale, true);
+    }
+    // online softmax per row stream, lazy reference max
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float cmax = s[0][g];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) cmax = fmaxf(cmax, s[i][g]);
+      if (cmax > m[g] + kLazyLog2) {
+        const float alpha = fast_exp2(m[g] - cmax);     // 0 while m = -inf
+        l[g] *= alpha;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
+        m[g] = cmax;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        // masked rows may still have m = -inf: select, do not subtract
+        const float pw = (!masked || s[i][g] > kNegInf) ? fast_exp2(s[i][g] - m[g]) : 0.f;
+        s[i][g] = pw;
+        l[g] += pw;
+      }
+    }
+    // value sums; masked rows may hold NaN-poisoned slots: zero them
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      Vec vv = vr[i];
+      if (has_app && i == i_app && row_app) vv = vn;
+      float vf[8];
+      widen8<FP8>(vv, vf);
+      if (masked && t0 + i * TPI + row >= s1) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vf[k] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pg = FP8 ? s[i][g] * vs[i] : s[i][g];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pg, vf[k], acc[g][k]);
+      }
+    }
+    if (j + 1 < my_n) issue(j + 1, vbase, vnew, vr, vn, vs, p.v_scale, false);
+  }
+
+  // Merge the TPI row streams of the wave (row r holds lanes r*LPT ..).
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mp = __shfl_xor(m[g], off, kWave);
+      const float lp = __shfl_xor(l[g], off, kWave);
+      const float M = fmaxf(m[g], mp);
+      const float a = m[g] > kNegInf ? fast_exp2(m[g] - M) : 0.f;
+      const float c = mp > kNegInf ? fast_exp2(mp - M) : 0.f;
+      l[g] = a * l[g] + c * lp;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[g][k] = a * acc[g][k] + c * __shfl_xor(acc[g][k], off, kWave);
+      m[g] = M;
+    }
+  }
+  const bool wave_bad = __any(bad);
+  if (row == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sm_acc(wave, g, col * 8 + k) = acc[g][k];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      sm_m[wave][g] = m[g];
+      sm_l[wave][g] = l[g];
+    }
+    sm_flag[wave] = wave_bad ? 1 : 0;
+  }
+  __syncthreads();
+
+  // Merge the waves: this split's normalised output and base-2 lse.
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) any_bad |= sm_flag[w];
+  const size_t prow = ((size_t)b * p.num_kv_heads + kvh) * p.max_splits;   // partial rows
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm_m[w][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float mw = sm_m[w][g];
+      const float a = mw > kNegInf ? fast_exp2(mw - M) : 0.f;
+      L = fmaf(a, sm_l[w][g], L);
+      O = fmaf(a, sm_acc(w, g, d), O);
+    }
+    const float o = O / L;
+    const float lse2 = any_bad ? __builtin_nanf("") : M + log2f(L);
+    if (nsplit == 1) {
+      p.out[((size_t)b * p.num_q_heads + h0 + g) * D + d] = any_bad ? __builtin_nanf("") : o;
+      if (p.out_lse && d == 0) p.out_lse[(size_t)b * p.num_q_heads + h0 + g] = lse2 * kLn2;
+    } else {
+      store_coherent(&p.ws_o[((prow + split) * G + g) * D + d], o);
+      if (d == 0) store_coherent(&p.ws_lse[(prow + split) * G + g], lse2);
+    }
+  }
+  if (nsplit == 1) return;
+
+  // Publish, count arrivals; the last workgroup of this (sequence, KV head) merges.
+  wait_vector_memory();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[(size_t)b * p.num_kv_heads + kvh],
+                                                 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_flag[WAVES] = prev == (uint32_t)(nsplit - 1);
+  }
+  __syncthreads();
+  if (!sm_flag[WAVES]) return;
+
+  // Split weights per head: w_s = 2^(lse_s - M) / sum, one wave per head.
+  float* sm_w = sm_buf;                            // [G][64]
+  float* sm_lse = sm_buf + G * kWave;              // [G] merged base-2 lse
+  float4* sm_red = reinterpret_cast<float4*>(sm_buf + G * kWave + 4 * ((G + 3) / 4));
+  for (int g = wave; g < G; g += WAVES) {
+    const float x = lane < nsplit ? load_coherent(&p.ws_lse[(prow + lane) * G + g]) : kNegInf;
+    const bool nan = __any(x != x);
+    const float M = wave_max(x);
+    const float w = lane < nsplit ? fast_exp2(x - M) : 0.f;
+    const float L = wave_sum(w);
+    sm_w[g * kWave + lane] = nan ? __builtin_nanf("") : w / L;
+    if (lane == 0) sm_lse[g] = nan ? __builtin_nanf("") : M + log2f(L);
+  }
+  __syncthreads();
+
+  // out[g][d] = sum_s w_s o_s[g][d] over float4 columns; SP threads share a
+  // column (splits part, part + SP, ...) and combine through LDS.
+  float4* outp = reinterpret_cast<float4*>(p.out + ((size_t)b * p.num_q_heads + h0) * D);
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_o + prow * G * D, 0, nsplit * G * D * 4, kBufferRsrcWord3);
+  const int part = NT >= C4 ? tid / C4 : 0;
+  for (int c = NT >= C4 ? tid % C4 : tid; c < C4; c += NT >= C4 ? C4 : NT) {
+    const int g = (c * 4) / D;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sb = part; sb < nsplit; sb += 8 * SP) {
+      float4 v[8];
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int si = sb + u * SP;
+        const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+            src, (si < nsplit ? si * C4 + c : 0) * 16, 0, kCachePolicySc1);
+        v[u] = si < nsplit ? make_float4(x.x, x.y, x.z, x.w) : make_float4(0.f, 0.f, 0.f, 0.f);
+        w[u] = si < nsplit ? sm_w[g * kWave + si] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        o.x = fmaf(w[u], v[u].x, o.x);
+        o.y = fmaf(w[u], v[u].y, o.y);
+        o.z = fmaf(w[u], v[u].z, o.z);
+        o.w = fmaf(w[u], v[u].w, o.w);
+      }
+    }
+    if constexpr (SP > 1) sm_red[part * C4 + c] = o;
+    else outp[c] = o;
+  }
+  if constexpr (SP > 1) {
+    __syncthreads();
+    for (int c = tid; c < C4; c += NT) {
+      float4 o = sm_red[c];
+#pragma unroll
+      for (int q = 1; q < SP; ++q) {
+        const float4 v = sm_red[q * C4 + c];
+        o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+      }
+      outp[c] = o;
+    }
+  }
+  if (p.out_lse && tid < G) p.out_lse[(size_t)b * p.num_q_heads + h0 + tid] = sm_lse[tid] * kLn2;
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[(size_t)b * p.num_kv_heads + kvh], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero the arrival counters of a workspace (used once, before its first call).
+__global__ void zero_words_kernel(uint32_t* w, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    w[i] = 0u;
+}
+
+}  // namespace gqa

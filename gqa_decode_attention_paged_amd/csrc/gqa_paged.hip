@@ -1,0 +1,316 @@
+// Host side of the paged GQA decode-attention library: argument validation,
+// workspace sizing, kernel selection and launches.  The C ABI is declared in
+// include/gqa_paged.h; the device code lives in the headers next to this file.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gqa_paged.h"
+#include "common.h"
+#include "decode_kernel.h"
+#include "kv_cache_ops.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kWaves = 4;
+
+gqa_status fail(gqa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gqa_status ok() {
+  g_last_error.clear();
+  return GQA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+gqa_status check_shape(const gqa_paged_shape* s) {
+  if (!s) return fail(GQA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->num_seqs < 0) return fail(GQA_ERR_INVALID_ARG, "num_seqs %d < 0", s->num_seqs);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(GQA_ERR_INVALID_ARG, "head counts must be >= 1 (H_q=%d, H_kv=%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(GQA_ERR_INVALID_ARG, "H_q=%d is not a multiple of H_kv=%d", s->num_q_heads,
+                s->num_kv_heads);
+  if (s->num_blocks < 1 || s->max_blocks_per_seq < 1)
+    return fail(GQA_ERR_INVALID_ARG, "num_blocks=%d and max_blocks_per_seq=%d must be >= 1",
+                s->num_blocks, s->max_blocks_per_seq);
+  if (s->head_dim < 1 || s->block_size < 1)
+    return fail(GQA_ERR_INVALID_ARG, "head_dim and block_size must be >= 1");
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(GQA_ERR_UNSUPPORTED, "group size G=%d not in {1,2,4,8}", G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "head_dim=%d not in {64,128}", s->head_dim);
+  if (s->block_size != 16 && s->block_size != 32)
+    return fail(GQA_ERR_UNSUPPORTED, "block_size=%d not in {16,32}", s->block_size);
+  if (s->kv_dtype != GQA_KV_BF16 && s->kv_dtype != GQA_KV_FP8_E4M3)
+    return fail(GQA_ERR_UNSUPPORTED, "kv_dtype=%d unknown", s->kv_dtype);
+  if ((int64_t)s->max_blocks_per_seq * s->block_size > INT32_MAX)
+    return fail(GQA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size overflows int32");
+  return GQA_OK;
+}
+
+struct WorkspaceLayout {
+  size_t o_off, lse_off, cnt_words, total;
+};
+
+// [counters: B*Hkv u32][partial outputs: B*Hkv*S*G*D fp32][partial lse: B*Hkv*S*G fp32]
+// The counters come first so that a workspace initialised for one shape serves
+// any later call with no more (sequence, KV head) pairs.
+WorkspaceLayout workspace_layout(const gqa_paged_shape* s, int max_splits) {
+  WorkspaceLayout w;
+  w.cnt_words = (size_t)s->num_seqs * s->num_kv_heads;
+  const size_t rows = (size_t)s->num_seqs * s->num_q_heads * (size_t)max_splits;
+  w.o_off = (w.cnt_words * sizeof(uint32_t) + 255) & ~size_t(255);
+  w.lse_off = (w.o_off + rows * s->head_dim * sizeof(float) + 255) & ~size_t(255);
+  w.total = w.lse_off + rows * sizeof(float);
+  return w;
+}
+
+int max_splits_for(int32_t max_context_len) {
+  const int ms = gqa::split_plan(max_context_len).num_splits;
+  return ms < 1 ? 1 : ms;
+}
+
+// Kernel dispatch over the supported (D, BS, G, dtype) combinations.
+template <int D, int BS, int G>
+const void* pick_kernel_g(bool fp8) {
+  return fp8 ? reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, true, kWaves>)
+             : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, false, kWaves>);
+}
+
+template <int D, int BS>
+const void* pick_kernel_bs(int G, bool fp8) {
+  switch (G) {
+    case 1: return pick_kernel_g<D, BS, 1>(fp8);
+    case 2: return pick_kernel_g<D, BS, 2>(fp8);
+    case 4: return pick_kernel_g<D, BS, 4>(fp8);
+    case 8: return pick_kernel_g<D, BS, 8>(fp8);
+  }
+  return nullptr;
+}
+
+const void* pick_kernel(int D, int BS, int G, bool fp8) {
+  if (D == 64) return BS == 16 ? pick_kernel_bs<64, 16>(G, fp8) : pick_kernel_bs<64, 32>(G, fp8);
+  return BS == 16 ? pick_kernel_bs<128, 16>(G, fp8) : pick_kernel_bs<128, 32>(G, fp8);
+}
+
+gqa_status launch(const void* fn, dim3 grid, dim3 block, void* params, const char* what,
+                  hipStream_t stream) {
+  void* args[] = {params};
+  hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+const char* gqa_version(void) { return "gqa_paged 0.2 (gfx950)"; }
+
+int32_t gqa_decode_num_splits(int32_t context_len) {
+  return gqa::split_plan(context_len).num_splits;
+}
+
+size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max_context_len) {
+  if (check_shape(shape) != GQA_OK || max_context_len < 0) return 0;
+  return workspace_layout(shape, max_splits_for(max_context_len)).total;
+}
+
+gqa_status gqa_kv_append(const gqa_paged_shape* s, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                         const int32_t* positions, hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (s->kv_dtype != GQA_KV_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "kv_append supports bf16 pools only");
+  if (s->num_seqs == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !positions)
+    return fail(GQA_ERR_INVALID_ARG, "kv_append: NULL device pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(GQA_ERR_INVALID_ARG, "kv_append: K/V pointers must be 16-byte aligned");
+  gqa::AppendParams p;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.positions = positions;
+  p.num_kv_heads = s->num_kv_heads;
+  p.head_dim = s->head_dim;
+  p.block_size = s->block_size;
+  p.num_blocks = s->num_blocks;
+  p.max_blocks = s->max_blocks_per_seq;
+  st = launch(reinterpret_cast<const void*>(&gqa::kv_append_kernel), dim3(s->num_seqs),
+              dim3(256), &p, "kv_append", stream);
+  return st == GQA_OK ? ok() : st;
+}
+
+static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_cache,
+                              void* v_cache, const float* k_scale, const float* v_scale,
+                              const void* k_new, const void* v_new, const int32_t* positions,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t max_context_len, float softmax_scale, float* out,
+                              float* out_lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (max_context_len < 0)
+    return fail(GQA_ERR_INVALID_ARG, "max_context_len %d < 0", max_context_len);
+  if ((int64_t)max_context_len > (int64_t)s->max_blocks_per_seq * s->block_size)
+    return fail(GQA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks_per_seq*block_size",
+                max_context_len);
+  if (!std::isfinite(softmax_scale))
+    return fail(GQA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const bool fp8 = s->kv_dtype == GQA_KV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale))
+    return fail(GQA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale))
+    return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
+  if (positions && fp8)
+    return fail(GQA_ERR_UNSUPPORTED, "the fused append supports bf16 pools only");
+  if (s->num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(GQA_ERR_INVALID_ARG, "decode: NULL device pointer");
+  if (positions && (!k_new || !v_new))
+    return fail(GQA_ERR_INVALID_ARG, "append: NULL k_new/v_new");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
+    return fail(GQA_ERR_INVALID_ARG, "decode: q, caches, new rows and out must be 16-byte aligned");
+  const int max_splits = max_splits_for(max_context_len);
+  const WorkspaceLayout wl = workspace_layout(s, max_splits);
+  if (!workspace || workspace_bytes < wl.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                wl.total);
+  if (!aligned16(workspace))
+    return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if ((int64_t)max_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
+    return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+
+  const int G = s->num_q_heads / s->num_kv_heads;
+  char* ws = static_cast<char*>(workspace);
+  gqa::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.positions = positions;
+  p.out = out;
+  p.out_lse = out_lse;
+  p.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+  p.ws_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+  p.counters = reinterpret_cast<uint32_t*>(ws);
+  p.num_q_heads = s->num_q_heads;
+  p.num_kv_heads = s->num_kv_heads;
+  p.num_blocks = s->num_blocks;
+  p.max_blocks = s->max_blocks_per_seq;
+  p.max_splits = max_splits;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8);
+  if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
+  st = launch(fn, dim3(max_splits, s->num_kv_heads, s->num_seqs), dim3(kWaves * 64), &p,
+              "paged_decode", stream);
+  return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_paged_decode_attention(const gqa_paged_shape* s, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t max_context_len, float softmax_scale, float* out,
+                                      float* out_lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  return decode_impl(s, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_scale,
+                     v_scale, nullptr, nullptr, nullptr, block_tables, context_lens,
+                     max_context_len, softmax_scale, out, out_lse, workspace, workspace_bytes,
+                     stream);
+}
+
+gqa_status gqa_paged_decode_append_attention(
+    const gqa_paged_shape* s, const void* q, const void* k_new, const void* v_new,
+    const int32_t* positions, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t max_context_len, float softmax_scale, float* out,
+    float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (s && s->num_seqs > 0 && !positions)
+    return fail(GQA_ERR_INVALID_ARG, "append: NULL positions");
+  return decode_impl(s, q, k_cache, v_cache, nullptr, nullptr, k_new, v_new, positions,
+                     block_tables, context_lens, max_context_len, softmax_scale, out, out_lse,
+                     workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* s, int32_t max_context_len,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (max_context_len < 0)
+    return fail(GQA_ERR_INVALID_ARG, "max_context_len %d < 0", max_context_len);
+  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len));
+  if (!workspace || workspace_bytes < wl.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                wl.total);
+  if (wl.cnt_words == 0) return ok();
+  uint32_t* cnt = static_cast<uint32_t*>(workspace);
+  size_t n = wl.cnt_words;
+  struct {
+    uint32_t* w;
+    size_t n;
+  } args{cnt, n};
+  void* argv[] = {&args.w, &args.n};
+  const unsigned blocks = (unsigned)((n + 255) / 256 > 1024 ? 1024 : (n + 255) / 256);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&gqa::zero_words_kernel),
+                                 dim3(blocks), dim3(256), argv, 0, stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "workspace init failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gqa_status gqa_kv_gather(const gqa_paged_shape* s, const void* cache, const int32_t* block_tables,
+                         int32_t seq, int32_t num_tokens, void* out, hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (seq < 0 || seq >= s->num_seqs)
+    return fail(GQA_ERR_INVALID_ARG, "seq %d out of range [0, %d)", seq, s->num_seqs);
+  if (num_tokens < 0 || (int64_t)num_tokens > (int64_t)s->max_blocks_per_seq * s->block_size)
+    return fail(GQA_ERR_INVALID_ARG, "num_tokens %d out of range", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!cache || !block_tables || !out) return fail(GQA_ERR_INVALID_ARG, "gather: NULL pointer");
+  if (!aligned16(cache) || !aligned16(out))
+    return fail(GQA_ERR_INVALID_ARG, "gather: pointers must be 16-byte aligned");
+  gqa::GatherParams p;
+  p.cache = static_cast<const char*>(cache);
+  p.block_table = block_tables + (size_t)seq * s->max_blocks_per_seq;
+  p.out = static_cast<char*>(out);
+  p.num_kv_heads = s->num_kv_heads;
+  p.block_size = s->block_size;
+  p.num_blocks = s->num_blocks;
+  p.num_tokens = num_tokens;
+  p.row_bytes = s->head_dim * (s->kv_dtype == GQA_KV_FP8_E4M3 ? 1 : 2);
+  st = launch(reinterpret_cast<const void*>(&gqa::kv_gather_kernel),
+              dim3((num_tokens + 63) / 64, s->num_kv_heads), dim3(256), &p, "kv_gather", stream);
+  return st == GQA_OK ? ok() : st;
+}
+
+}  // extern "C"

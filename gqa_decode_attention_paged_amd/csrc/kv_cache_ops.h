@@ -1,0 +1,79 @@
+// KV append (commit one new token per sequence) and a block-table gather.
+//
+// Cites: *LLM Inference Systems Engineering* (jasonzhang109) §2.1.3 — a decode
+// step first writes the pending token's K/V into the cache, then attends;
+// *The Mathematics of Transformer Inference* (hs-black) §1 — decode appends the
+// new token's own K and V; *Module 10: Inference and Deployment Serving*
+// (wrwei.github.io), "Mapping logical positions to physical blocks" — token t
+// lives in physical block table[t / BS] at slot t % BS.
+//
+// Both are plain byte copies in 16-byte units (bit-exact).
+#pragma once
+
+#include "common.h"
+
+namespace gqa {
+
+struct AppendParams {
+  const uint16_t* k_new;        // [B][Hkv][D]
+  const uint16_t* v_new;
+  uint16_t* k_cache;            // [NB][Hkv][BS][D]
+  uint16_t* v_cache;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* positions;     // [B]
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks;
+};
+
+// grid: B workgroups; each thread copies 16 B units of the K and V rows.
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
+  const int b = blockIdx.x;
+  const int pos = p.positions[b];
+  if (pos < 0 || pos >= p.max_blocks * p.block_size) return;
+  const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / p.block_size];
+  if (blk < 0 || blk >= p.num_blocks) return;
+  const int slot = pos % p.block_size;
+  const int upr = p.head_dim / 8;                    // 16 B units per row
+  for (int u = threadIdx.x; u < p.num_kv_heads * upr; u += blockDim.x) {
+    const int h = u / upr;
+    const int c = u % upr;
+    const size_t src = ((size_t)b * p.num_kv_heads + h) * p.head_dim + c * 8;
+    const size_t dst = (((size_t)blk * p.num_kv_heads + h) * p.block_size + slot) * p.head_dim + c * 8;
+    *reinterpret_cast<uint4*>(p.k_cache + dst) = *reinterpret_cast<const uint4*>(p.k_new + src);
+    *reinterpret_cast<uint4*>(p.v_cache + dst) = *reinterpret_cast<const uint4*>(p.v_new + src);
+  }
+}
+
+struct GatherParams {
+  const char* cache;            // [NB][Hkv][BS][row_bytes]
+  const int32_t* block_table;   // row of the sequence
+  char* out;                    // [Hkv][num_tokens][row_bytes]
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t num_tokens;
+  int32_t row_bytes;            // head_dim * element size (multiple of 16)
+};
+
+// grid: (ceil(num_tokens / 64), Hkv); 256 threads copy 16 B units of 64 rows.
+__global__ __launch_bounds__(256) void kv_gather_kernel(GatherParams p) {
+  const int h = blockIdx.y;
+  const int upr = p.row_bytes / 16;
+  const int t0 = blockIdx.x * 64;
+  for (int u = threadIdx.x; u < 64 * upr; u += blockDim.x) {
+    const int t = t0 + u / upr;
+    const int c = u % upr;
+    if (t >= p.num_tokens) continue;
+    const int blk = p.block_table[t / p.block_size];
+    if (blk < 0 || blk >= p.num_blocks) continue;
+    const size_t src = (((size_t)blk * p.num_kv_heads + h) * p.block_size + t % p.block_size) *
+                           (size_t)p.row_bytes + (size_t)c * 16;
+    const size_t dst = ((size_t)h * p.num_tokens + t) * (size_t)p.row_bytes + (size_t)c * 16;
+    *reinterpret_cast<uint4*>(p.out + dst) = *reinterpret_cast<const uint4*>(p.cache + src);
+  }
+}
+
+}  // namespace gqa

@@ -1,0 +1,216 @@
+/*
+ * gqa_paged.h — C ABI of the MI355X (gfx950) paged GQA decode-attention library.
+ *
+ * The library computes single-token decode attention over a paged KV cache with
+ * grouped query heads, and the KV append that commits a new token before it.
+ *
+ * What the operations are, and where the pages state them:
+ *  - KV cache and append: each step commits the pending token's K/V, then its
+ *    query attends over the cache including itself.  *LLM Inference Systems
+ *    Engineering* (jasonzhang109) §2.1.3; *The Mathematics of Transformer
+ *    Inference* (hs-black) §1.
+ *  - Paging: fixed-size physical blocks in one shared pool, a per-sequence block
+ *    table from logical to physical block; a sequence's blocks need not be
+ *    adjacent; the attention kernel reads K/V through the table and only reads
+ *    each sequence's valid tokens.  *Module 10: Inference and Deployment Serving*
+ *    (wrwei.github.io), "Mapping logical positions to physical blocks";
+ *    *The Mathematics of Transformer Inference* §9 (PagedAttention).
+ *  - Decode attention with grouped queries: query head h reads KV head
+ *    floor(h / G), G = H_q / H_kv; scores are softmax_scale * <q, k>, the output
+ *    is the softmax-weighted sum of values.  *The Mathematics of Transformer
+ *    Inference* §4-5; *Module 10*, Lab 2 (KV heads repeated over consecutive
+ *    query heads).
+ *  - FP8 KV: E4M3 in the finite-only convention (max 448), dequantised inside the
+ *    kernel with a scale.  *Module 10*, number-format table; *The Mathematics of
+ *    Transformer Inference* §11.
+ *
+ * Conventions shared by all calls
+ *  - All pointers except `shape` are DEVICE pointers on the current HIP device,
+ *    owned by the caller.  The library allocates nothing and keeps no device
+ *    state between calls.  Every call is asynchronous on `stream` (0 = null
+ *    stream) and only enqueues work; results are ready when the stream is.
+ *  - bf16 values are raw bfloat16 bit patterns (uint16); fp8 values are OCP
+ *    E4M3 codes (uint8; 0x7F/0xFF are NaN, no infinity).
+ *  - KV pool layout: k_cache, v_cache are [num_blocks][num_kv_heads][block_size][head_dim]
+ *    (row-major), so one (block, KV head) tile is contiguous.  Token t of sequence b
+ *    lives in physical block block_tables[b * max_blocks_per_seq + t / block_size]
+ *    at slot t % block_size.  Table entries at or beyond ceil(ctx_b / block_size)
+ *    are never read.
+ *  - Supported shapes: head_dim in {64, 128}; block_size in {16, 32};
+ *    num_q_heads % num_kv_heads == 0 with G = num_q_heads / num_kv_heads in
+ *    {1, 2, 4, 8}; kv_dtype BF16 or FP8_E4M3.  Anything else returns
+ *    GQA_ERR_UNSUPPORTED.  Device pointers must be 16-byte aligned.
+ *  - Errors: a call validates its host-side arguments and returns a status; it
+ *    never aborts.  gqa_last_error() gives a message for the last non-OK status
+ *    on the calling thread.  Device-resident values (block ids, positions,
+ *    context lengths) are checked inside the kernels: a sequence whose context
+ *    length or attended block ids are out of range gets NaN in every output
+ *    element and lse of its heads (nothing outside the buffers is read), and an
+ *    append whose position or block id is out of range writes nothing.
+ */
+#ifndef GQA_PAGED_H
+#define GQA_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misaligned pointer  */
+  GQA_ERR_UNSUPPORTED = 2,   /* valid but unsupported head_dim/block_size/G/dtype */
+  GQA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required        */
+  GQA_ERR_HIP = 4            /* a HIP launch failed; see gqa_last_error()         */
+} gqa_status;
+
+typedef enum gqa_kv_dtype {
+  GQA_KV_BF16 = 0,
+  GQA_KV_FP8_E4M3 = 1
+} gqa_kv_dtype;
+
+/* Host-side description of one paged KV cache and one batch of sequences. */
+typedef struct gqa_paged_shape {
+  int32_t num_seqs;            /* B: sequences in the batch (0 is a no-op)           */
+  int32_t num_q_heads;         /* H_q                                                 */
+  int32_t num_kv_heads;        /* H_kv; H_q % H_kv == 0                               */
+  int32_t head_dim;            /* d_h                                                 */
+  int32_t block_size;          /* BS tokens per physical block                        */
+  int32_t num_blocks;          /* physical blocks in each pool                        */
+  int32_t max_blocks_per_seq;  /* row length of block_tables                          */
+  int32_t kv_dtype;            /* gqa_kv_dtype                                        */
+} gqa_paged_shape;
+
+/*
+ * gqa_kv_append — commit one new token per sequence into the paged pools.
+ *   k_new, v_new  [B][H_kv][d_h] bf16       the token's key and value rows
+ *   k_cache, v_cache  pools (layout above), modified in place
+ *   block_tables  [B][max_blocks_per_seq] int32
+ *   positions     [B] int32: logical slot to write (usually ctx_b - 1, the new
+ *                 token's index); a negative position skips that sequence
+ * Writes k_cache[blk][h][pos % BS][:] = k_new[b][h][:] (same for V) with
+ * blk = block_tables[b][pos / BS]; a bit-exact copy.  context_lens is not
+ * touched: the caller passes the grown length to the attention call.
+ * bf16 pools only (FP8 append returns GQA_ERR_UNSUPPORTED).
+ */
+gqa_status gqa_kv_append(const gqa_paged_shape* shape,
+                         const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache,
+                         const int32_t* block_tables, const int32_t* positions,
+                         hipStream_t stream);
+
+/*
+ * gqa_decode_num_splits — the context split policy (host function, no GPU).
+ * Returns how many partial attentions a sequence of `context_len` tokens is cut
+ * into.  It depends on that sequence's own length only, so a sequence's result
+ * does not depend on the rest of the batch.  0 for context_len <= 0.
+ */
+int32_t gqa_decode_num_splits(int32_t context_len);
+
+/*
+ * gqa_paged_decode_workspace_size — bytes of device workspace that
+ * gqa_paged_decode_attention needs for this shape when no sequence is longer
+ * than max_context_len.  Returns 0 for invalid or unsupported arguments.
+ */
+size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max_context_len);
+
+/*
+ * gqa_paged_decode_attention — one decode step of attention for B sequences.
+ *   q             [B][H_q][d_h] bf16
+ *   k_cache, v_cache  pools (layout above); bf16 or fp8 codes
+ *   k_scale, v_scale  [num_blocks][H_kv] fp32 dequantisation scales for fp8
+ *                 pools (value = decode(code) * scale[block][kv_head]); must
+ *                 be NULL for bf16
+ *   block_tables  [B][max_blocks_per_seq] int32
+ *   context_lens  [B] int32: tokens each sequence attends, including a token
+ *                 just appended; 0 gives out = 0, lse = -inf
+ *   max_context_len  host bound on every context_lens[b]; sizes the launch.
+ *                 A sequence longer than this gets NaN output.
+ *   softmax_scale score multiplier (usually 1/sqrt(d_h))
+ *   out           [B][H_q][d_h] fp32 (written)
+ *   out_lse       [B][H_q] fp32 natural-log log-sum-exp of the scores, or NULL
+ *   workspace     device scratch of at least
+ *                 gqa_paged_decode_workspace_size(shape, max_context_len) bytes,
+ *                 16-byte aligned.  It starts with one arrival counter (u32) per
+ *                 (sequence, KV head), followed by the partial results of the
+ *                 context splits.  The first B*H_kv words must be zero before a
+ *                 call (gqa_paged_decode_workspace_init, or any zero fill); every
+ *                 call leaves them zero again, so a workspace prepared once serves
+ *                 any later call with no more (sequence, KV head) pairs.  One
+ *                 workspace serves one call at a time: calls sharing it must be
+ *                 ordered on one stream.
+ * Inputs are read only.  One kernel runs on `stream`: each workgroup attends
+ * over one context split of one (sequence, KV head); the last workgroup of a
+ * (sequence, KV head) to finish merges the splits by log-sum-exp.
+ */
+gqa_status gqa_paged_decode_attention(const gqa_paged_shape* shape,
+                                      const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_tables,
+                                      const int32_t* context_lens,
+                                      int32_t max_context_len,
+                                      float softmax_scale,
+                                      float* out, float* out_lse,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/*
+ * gqa_paged_decode_append_attention — one fused decode step ("forward and
+ * commit"): write each sequence's new token into the cache, then attend over
+ * context_lens[b] tokens that include it, in a single kernel.
+ *   k_new, v_new  [B][H_kv][d_h] bf16 new rows; positions [B] int32 slot of the
+ *                 new token (normally context_lens[b] - 1; negative = no append)
+ *   other arguments as gqa_paged_decode_attention (k_cache/v_cache are written
+ *   at the appended slots only).  Same results as gqa_kv_append followed by
+ *   gqa_paged_decode_attention.  bf16 pools only (fp8: GQA_ERR_UNSUPPORTED).
+ * Cites: *LLM Inference Systems Engineering* §2.1.3 (each step commits the
+ * pending token's K/V, then attends over the cache that includes it).
+ */
+gqa_status gqa_paged_decode_append_attention(const gqa_paged_shape* shape,
+                                             const void* q,
+                                             const void* k_new, const void* v_new,
+                                             const int32_t* positions,
+                                             void* k_cache, void* v_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens,
+                                             int32_t max_context_len,
+                                             float softmax_scale,
+                                             float* out, float* out_lse,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+
+/*
+ * gqa_paged_decode_workspace_init — zero the arrival counters (the first
+ * B*H_kv words) of a workspace sized for (shape, max_context_len).  Enqueued on
+ * `stream` as a small fill kernel (no memset), so it may be captured in a HIP
+ * graph.
+ */
+gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t max_context_len,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
+/*
+ * gqa_kv_gather — copy the first num_tokens cached rows of sequence `seq` out
+ * of one pool into a contiguous [H_kv][num_tokens][d_h] array (element width
+ * of the pool), in logical order.  A bit-exact indexing check of the paged
+ * layout; not on the decode path.
+ */
+gqa_status gqa_kv_gather(const gqa_paged_shape* shape, const void* cache,
+                         const int32_t* block_tables, int32_t seq, int32_t num_tokens,
+                         void* out, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* gqa_last_error(void);
+
+/* Library version string. */
+const char* gqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_PAGED_H */

@@ -1,0 +1,151 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol,
+and its host-side logic (split policy, workspace size, argument validation)
+behaves as documented.  No call here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_paged.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gqa_decode_attention_paged_amd as gqa
+    from gqa_decode_attention_paged_amd import build
+    if not os.path.exists(gqa.LIB_PATH):
+        build.build()
+    return gqa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gqa_kv_append", "gqa_paged_decode_attention",
+                     "gqa_paged_decode_workspace_size", "gqa_last_error"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _shape(**kw):
+    from gqa_decode_attention_paged_amd import PagedShape
+    base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                num_blocks=1024, max_blocks_per_seq=600, kv_dtype=0)
+    base.update(kw)
+    return PagedShape(**base)
+
+
+def test_split_policy(lib):
+    import gqa_decode_attention_paged_amd as gqa
+    assert gqa.num_splits(0) == 0 and gqa.num_splits(-5) == 0
+    assert gqa.num_splits(1) == 1 and gqa.num_splits(128) == 1 and gqa.num_splits(129) == 2
+    assert gqa.num_splits(8192) == 64
+    assert gqa.num_splits(32769) <= 64
+    prev = 0
+    for ctx in range(0, 20000, 37):
+        n = gqa.num_splits(ctx)
+        assert 0 <= n <= 64
+        assert n >= (1 if ctx > 0 else 0)
+        prev = n
+    assert prev > 0
+
+
+def test_workspace_size_formula(lib):
+    import gqa_decode_attention_paged_amd as gqa
+    s = _shape()
+    ms = gqa.num_splits(8192)
+    rows = 2 * 32 * ms
+    o_off = (2 * 8 * 4 + 255) // 256 * 256          # counters come first
+    lse_off = (o_off + rows * 128 * 4 + 255) // 256 * 256
+    assert gqa.workspace_size(s, 8192) == lse_off + rows * 4
+    assert gqa.workspace_size(_shape(head_dim=96), 8192) == 0      # unsupported
+    assert gqa.workspace_size(s, -1) == 0
+
+
+def _call_decode(lib, shape, ws_bytes=1 << 30, ptr=16, **over):
+    args = dict(q=ptr, k=ptr, v=ptr, ks=None, vs=None, bt=ptr, ctx=ptr, max_ctx=100,
+                scale=0.1, out=ptr, lse=None, ws=ptr, ws_bytes=ws_bytes)
+    args.update(over)
+    P = ctypes.c_void_p
+    return lib.gqa_paged_decode_attention(
+        ctypes.byref(shape), P(args["q"]), P(args["k"]), P(args["v"]), P(args["ks"]),
+        P(args["vs"]), P(args["bt"]), P(args["ctx"]), args["max_ctx"], args["scale"],
+        P(args["out"]), P(args["lse"]), P(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), 2), (dict(block_size=8), 2), (dict(num_q_heads=24), 2),
+    (dict(num_q_heads=30), 1), (dict(num_seqs=-1), 1), (dict(kv_dtype=7), 2),
+    (dict(num_blocks=0), 1),
+])
+def test_decode_rejects_bad_shapes(lib, over, status):
+    assert _call_decode(lib, _shape(**over)) == status
+    assert lib.gqa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(ws=None), 3), (dict(ws_bytes=10), 3),
+    (dict(q=17), 1), (dict(max_ctx=-1), 1), (dict(max_ctx=10 ** 6), 1),
+    (dict(scale=float("nan")), 1), (dict(ks=16), 1),
+])
+def test_decode_rejects_bad_arguments(lib, over, status):
+    assert _call_decode(lib, _shape(), **over) == status
+
+
+def test_fp8_needs_scales(lib):
+    assert _call_decode(lib, _shape(kv_dtype=1)) == 1
+
+
+def test_zero_sequences_return_ok_without_launching(lib):
+    assert _call_decode(lib, _shape(num_seqs=0)) == 0
+
+
+def test_fused_append_validation(lib):
+    P = ctypes.c_void_p
+    s = _shape()
+    call = lambda shape, pos, kn: lib.gqa_paged_decode_append_attention(
+        ctypes.byref(shape), P(16), P(kn), P(16), P(pos), P(16), P(16), P(16), P(16), 100, 0.1,
+        P(16), None, P(16), 1 << 30, None)
+    assert call(s, None, 16) == 1                     # positions required
+    assert call(s, 16, None) == 1                     # new rows required
+    assert call(_shape(kv_dtype=1), 16, 16) in (1, 2)  # fp8 pools: no fused append
+    assert call(_shape(num_seqs=0), None, None) == 0
+
+
+def test_workspace_init_validation(lib):
+    P = ctypes.c_void_p
+    s = _shape()
+    assert lib.gqa_paged_decode_workspace_init(ctypes.byref(s), 100, None, 0, None) == 3
+    assert lib.gqa_paged_decode_workspace_init(ctypes.byref(s), -1, P(16), 1 << 20, None) == 1
+
+
+def test_append_validation(lib):
+    P = ctypes.c_void_p
+    s = _shape(kv_dtype=1)
+    assert lib.gqa_kv_append(ctypes.byref(s), P(16), P(16), P(16), P(16), P(16), P(16), None) == 2
+    s = _shape()
+    assert lib.gqa_kv_append(ctypes.byref(s), None, P(16), P(16), P(16), P(16), P(16), None) == 1
+    assert lib.gqa_kv_append(None, P(16), P(16), P(16), P(16), P(16), P(16), None) == 1
+
+
+def test_gather_validation(lib):
+    P = ctypes.c_void_p
+    s = _shape()
+    assert lib.gqa_kv_gather(ctypes.byref(s), P(16), P(16), 5, 10, P(16), None) == 1
+    assert lib.gqa_kv_gather(ctypes.byref(s), P(16), P(16), 0, -1, P(16), None) == 1
+    assert lib.gqa_kv_gather(ctypes.byref(s), P(16), P(16), 0, 0, P(16), None) == 0
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.gqa_version()

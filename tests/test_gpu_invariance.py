@@ -1,0 +1,66 @@
+"""GPU invariants: physical placement, batch composition, fp8 code decoding."""
+import numpy as np
+import pytest
+
+import oracle
+from tests._dev import to_device, run_step
+from workloads import make_case, small_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def test_block_permutation_is_bit_identical(gpu):
+    """Results follow logical positions, not where blocks sit in the pool."""
+    spec = small_spec(num_seqs=3, num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                      context=("uniform", 100, 3000), case_id=4000)
+    case = make_case(spec, seed=1)
+    out, lse = run_step(gpu, to_device(case), case)
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(case["k_pool"].shape[0])
+    moved = dict(case)
+    for key in ("k_pool", "v_pool"):
+        moved[key] = np.empty_like(case[key])
+        moved[key][perm] = case[key]
+    bt = case["block_tables"].copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    moved["block_tables"] = bt
+    out2, lse2 = run_step(gpu, to_device(moved), moved)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_batch_invariance_bitwise(gpu):
+    """A sequence gives the same bits alone, in a batch, and at another batch index."""
+    spec = small_spec(num_seqs=6, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context=("uniform", 1, 9000), case_id=4001)
+    case = make_case(spec, seed=2)
+    hint = case["block_tables"].shape[1] * 16          # the largest length the tables allow
+    out, lse = run_step(gpu, to_device(case), case, max_context_len=hint)
+    for b in (0, 3, 5):
+        one = dict(case)
+        one["q"] = case["q"][b:b + 1]
+        one["block_tables"] = case["block_tables"][b:b + 1]
+        one["context_lens"] = case["context_lens"][b:b + 1]
+        one["positions"] = case["positions"][b:b + 1]
+        o1, l1 = run_step(gpu, to_device(one), one)          # smaller launch hint
+        assert np.array_equal(o1[0], out[b]) and np.array_equal(l1[0], lse[b])
+    rev = dict(case)
+    for key in ("q", "block_tables", "context_lens", "positions"):
+        rev[key] = np.ascontiguousarray(case[key][::-1])
+    o2, l2 = run_step(gpu, to_device(rev), rev, max_context_len=hint)
+    assert np.array_equal(o2[::-1], out) and np.array_equal(l2[::-1], lse)
+
+
+def test_fp8_codes_decode_exactly(gpu):
+    """ctx = 1 makes out = decode(code) * scale exactly: all 254 finite codes."""
+    spec = small_spec(num_seqs=1, num_q_heads=2, num_kv_heads=2, head_dim=128, block_size=16,
+                      kv_dtype="fp8", context=1, pool="exact", case_id=4002)
+    case = make_case(spec, seed=3)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    codes = np.concatenate([codes, codes[:2]])                   # 256 values, 2 heads x 128
+    blk = case["block_tables"][0, 0]
+    for pool in ("v_pool", "v_pool_full"):
+        case[pool][blk, :, 0, :] = codes.reshape(2, 128)
+    case["v_scale"][blk, :] = np.float32(1.0)
+    out, _ = run_step(gpu, to_device(case), case)
+    want = oracle.decode_e4m3fn(codes).reshape(2, 128)
+    assert np.array_equal(out[0], want)
