@@ -68,6 +68,7 @@ struct DecodeParams {
   int32_t num_blocks;
   int32_t max_blocks;
   int32_t max_splits;
+  int32_t hint_ctx;             // host bound on context lengths (sizes the grid)
   float scale_log2;             // softmax_scale * log2(e)
 };
 
@@ -160,6 +161,47 @@ __device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kv
       *reinterpret_cast<const uint4*>(p.v_new + src);
 }
 
+// Cross-lane reductions.  `ror<N>`: rotate within each 16-lane row (DPP);
+// `swap16`/`swap32`: exchange rows 0<->1, 2<->3 / halves (gfx950 permlane swaps).
+template <int N>
+__device__ __forceinline__ float ror(float x) { return dpp<0x120 + N>(x); }
+
+__device__ __forceinline__ float max_swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_swap16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_swap16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max / sum over the lanes l' = l (mod M) of the wave (M = 1, 2, 4, 8, 16); every
+// lane receives the result for its own class.
+template <int M>
+__device__ __forceinline__ float class_max(float x) {
+  if constexpr (M <= 1) x = fmaxf(x, ror<1>(x));
+  if constexpr (M <= 2) x = fmaxf(x, ror<2>(x));
+  if constexpr (M <= 4) x = fmaxf(x, ror<4>(x));
+  if constexpr (M <= 8) x = fmaxf(x, ror<8>(x));
+  return max_swap32(max_swap16(x));
+}
+template <int M>
+__device__ __forceinline__ float class_sum(float x) {
+  if constexpr (M <= 1) x += ror<1>(x);
+  if constexpr (M <= 2) x += ror<2>(x);
+  if constexpr (M <= 4) x += ror<4>(x);
+  if constexpr (M <= 8) x += ror<8>(x);
+  return sum_swap32(sum_swap16(x));
+}
+
 template <int D, int BS, int G, bool FP8, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParams p) {
   constexpr int LPT = D / 8;                 // lanes per token row
@@ -170,13 +212,22 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   constexpr int CPG = kWave / EPC;           // chunks per preloaded table group
   constexpr int ESZ = KVTraits<FP8>::kBytes;
   constexpr int NT = WAVES * kWave;
+  constexpr int NPAIR = CT * G;              // (token, head) scores per chunk
+  constexpr int PPL = (NPAIR + kWave - 1) / kWave;   // scores per lane
+  constexpr int TSTEP = kWave / G;           // token stride between a lane's scores
+  // LDS score transpose: partial dot products of token t, head g, lane column c
+  // at t*PSTR + g*GSTR + c; the weights p[t][g] at t*G + g.
+  constexpr int GSTR = LPT + 4;
+  constexpr int PSTR = G * GSTR + 4;
+  constexpr int kPartFloats = CT * PSTR;
+  constexpr int kWaveFloats = kPartFloats + NPAIR + 4 * ((G + 3) / 4);
   static_assert(BS % TPI == 0 && kChunkTokens % CT == 0, "tile geometry");
+  static_assert(kWave % G == 0 && PPL * TSTEP * G >= NPAIR, "score mapping");
   using Vec = typename KVTraits<FP8>::Vec;
 
   // Workgroup -> (split, KV head, sequence).  When the number of (sequence,
   // KV head) pairs is a multiple of 8, all splits of one pair are placed on
-  // one XCD (workgroups are dealt to the 8 XCDs round robin), so the partial
-  // results the last workgroup merges stay in that XCD's L2.
+  // one XCD (workgroups are dealt to the 8 XCDs round robin).
   const int S = gridDim.x;
   const int P = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + S * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -195,22 +246,46 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform per wave
   const int row = lane / LPT;
   const int col = lane % LPT;
 
-  // LDS: per-wave partial sums during the split merge, then (reused) the split
-  // weights and float4 partial sums of the final merge.
+  // LDS: per-wave score transpose during the chunk loop; afterwards (reused) the
+  // per-wave partial sums, then the split weights and float4 sums of the merge.
   constexpr int C4 = G * D / 4;                    // float4 columns of one head group
   constexpr int SP = NT >= C4 ? NT / C4 : 1;       // threads per column in the final merge
   constexpr int kAccFloats = WAVES * G * D;
   constexpr int kMergeFloats = G * kWave + 4 * ((G + 3) / 4) + 4 * SP * C4;
-  constexpr int kBufFloats = kAccFloats > kMergeFloats ? kAccFloats : kMergeFloats;
+  constexpr int kLoopFloats = WAVES * kWaveFloats;
+  constexpr int kBufA = kAccFloats > kMergeFloats ? kAccFloats : kMergeFloats;
+  constexpr int kBufFloats = kBufA > kLoopFloats ? kBufA : kLoopFloats;
   __shared__ __attribute__((aligned(16))) float sm_buf[kBufFloats];
   __shared__ float sm_m[WAVES][G];
   __shared__ float sm_l[WAVES][G];
   __shared__ int sm_flag[WAVES + 1];
   auto sm_acc = [&](int w, int g, int d) -> float& { return sm_buf[(w * G + g) * D + d]; };
+  float* sm_part = sm_buf + wave * kWaveFloats;    // this wave's transpose area
+  float* sm_pw = sm_part + kPartFloats;            // [CT][G] weights
+  float* sm_alpha = sm_pw + NPAIR;                 // [G] rescale factors
+
+  // Speculative block-id prefetch: most batches have every sequence at the
+  // launch hint's length, so the ids of this wave's chunks under the hint's
+  // split plan are loaded together with the context length.
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks;
+  auto load_ids = [&](int s0_, int s1_, int my_n_, int jbase) {
+    const int jj = jbase + lane / EPC;
+    const int tok = s0_ + (wave + jj * WAVES) * CT + (lane % EPC) * BS;
+    return (jj < my_n_ && tok < s1_) ? bt[tok / BS] : 0;
+  };
+  auto wave_chunks = [&](int s0_, int s1_) {
+    const int nch = (s1_ - s0_ + CT - 1) / CT;
+    return wave < nch ? (nch - wave + WAVES - 1) / WAVES : 0;
+  };
+  const SplitPlan hplan = split_plan(p.hint_ctx);
+  const int hs0 = split * hplan.split_tokens;
+  const int hs1 = min(p.hint_ctx, hs0 + hplan.split_tokens);
+  const int hmy_n = split < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
+  int ids = load_ids(hs0, hs1, hmy_n, 0);
 
   const int ctx = p.context_lens[b];
   const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS;
@@ -219,7 +294,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   const int pos = p.positions ? p.positions[b] : -1;
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
   const int owner = (!degenerate && pos >= 0 && pos < ctx) ? pos / plan.split_tokens : 0;
-  if (p.positions && split == owner) append_rows(p, b, kvh, pos, D, BS);
+  const bool pos_in_split = !degenerate && pos >= 0 && pos < ctx;
+  if (p.positions && split == owner && !pos_in_split) append_rows(p, b, kvh, pos, D, BS);
 
   if (degenerate) {
     if (split != 0) return;
@@ -235,7 +311,28 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   if (split >= nsplit) return;
   const int s0 = split * plan.split_tokens;
   const int s1 = min(ctx, s0 + plan.split_tokens);
-  const int app = (pos >= s0 && pos < s1) ? pos : -1;     // appended token read from k_new
+  const int app = (pos >= s0 && pos < s1) ? pos : -1;    // appended token of this split
+  const int my_n = wave_chunks(s0, s1);
+  if (app >= 0) {
+    // The wave whose chunk holds the new token commits its K/V rows and waits
+    // for the stores, so its loads then read the token back from the cache.
+    const int c_app = (app - s0) / CT;
+    if (c_app % WAVES == wave) {
+      if (row == 0) {
+        const size_t src = ((size_t)b * p.num_kv_heads + kvh) * D + col * 8;
+        const int blk = bt[app / BS];
+        if ((unsigned)blk < (unsigned)p.num_blocks) {
+          const size_t dst = (((size_t)blk * p.num_kv_heads + kvh) * BS + app % BS) * D + col * 8;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + dst) =
+              *reinterpret_cast<const uint4*>(p.k_new + src);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + dst) =
+              *reinterpret_cast<const uint4*>(p.v_new + src);
+        }
+      }
+      wait_vector_memory();
+    }
+  }
+  if (s0 != hs0 || s1 != hs1) ids = load_ids(s0, s1, my_n, 0);   // hint did not apply
 
   // q: this lane's 8 dims of each of the G heads.
   const uint16_t* qp = p.q + ((size_t)b * p.num_q_heads + h0) * D + col * 8;
@@ -254,97 +351,88 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     }
   }
 
-  float m[G], l[G], acc[G][8];
+  // Online-softmax state.  The reference max m is wave-uniform per head (all
+  // rows share it), l is this lane's share of the exponential sum of its
+  // scores (head lane % G), acc the value sums of this lane's 8 dims.
+  const int sg = lane % G;                         // head of this lane's scores
+  float m_ref = kNegInf, l_part = 0.f;
+  float acc[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
-  }
   bool bad = false;
 
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks;
   const char* kbase = static_cast<const char*>(p.k_cache);
   const char* vbase = static_cast<const char*>(p.v_cache);
   constexpr size_t kTileBytes = (size_t)BS * D * ESZ;
   const size_t block_stride = (size_t)p.num_kv_heads * kTileBytes;
-  const size_t new_off = ((size_t)b * p.num_kv_heads + kvh) * D * 2 + (size_t)col * 16;
-
-  const int nchunks = (s1 - s0 + CT - 1) / CT;
-  const int my_n = wave < nchunks ? (nchunks - wave + WAVES - 1) / WAVES : 0;
-
-  // Block ids of this wave's chunks j0 .. j0+CPG-1: lane = (j - j0) * EPC + e.
   int j0 = 0;
-  auto load_ids = [&](int jbase) {
-    const int jj = jbase + lane / EPC;
-    const int tok = s0 + (wave + jj * WAVES) * CT + (lane % EPC) * BS;
-    return (jj < my_n && tok < s1) ? bt[tok / BS] : 0;
-  };
-  int ids = load_ids(0);
 
   // Instruction i of chunk j reads TPI rows of one (block, KV head) tile: a
   // wave-uniform tile base (block id via readlane) plus this lane's 16 B slot.
   const uint32_t lane_off = (uint32_t)lane * 8 * ESZ;
-  auto tile_base = [&](int j, int i, const char* pool, bool track) -> const char* {
+  auto block_id = [&](int j, int i) {
     const int e = CT >= BS ? (i * TPI) / BS : 0;
-    int phys = __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e);
+    return __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e);
+  };
+  // One (block, KV head) tile as a buffer resource: the block id is wave-uniform,
+  // so the base lives in scalar registers and each lane adds its 32-bit offset.
+  auto tile_rsrc = [&](int j, int i, const char* pool, bool track) {
+    int phys = block_id(j, i);
     const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
     if (track) bad |= !ok;
     phys = ok ? phys : 0;
-    const int first = (s0 + (wave + j * WAVES) * CT + i * TPI) % BS;   // uniform
-    return pool + (size_t)phys * block_stride + (size_t)kvh * kTileBytes +
-           (size_t)first * D * ESZ;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(pool) + (size_t)phys * block_stride + (size_t)kvh * kTileBytes, 0,
+        (int)kTileBytes, kBufferRsrcWord3);
   };
   auto chunk_start = [&](int j) { return s0 + (wave + j * WAVES) * CT; };
 
   // Issue the loads of one tile (K or V) of chunk j.  Branch-free: every row
   // reads an in-bounds slot (rows past the split end read their block's unused
-  // slots, whole groups past it read block 0) and compute masks them.  If the
-  // chunk holds the appended token, its row is also loaded from the new-token
-  // buffer into `nr`, and compute swaps it in.
-  auto issue = [&](int j, const char* pool, const char* nbase, Vec (&r)[NI], Vec& nr,
-                   float (&sc)[NI], const float* scales, bool track) {
+  // slots, whole groups past it read block 0) and compute masks them.
+  auto issue = [&](int j, const char* pool, Vec (&r)[NI], float (&sc)[NI],
+                   const float* scales, bool track) {
+    const int t0 = chunk_start(j);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      r[i] = *reinterpret_cast<const Vec*>(tile_base(j, i, pool, track) + lane_off);
+      const auto rsrc = tile_rsrc(j, i, pool, track);
+      const int first = (t0 + i * TPI) % BS;       // first row of this instruction, uniform
       if constexpr (FP8) {
-        const int e = CT >= BS ? (i * TPI) / BS : 0;
-        int phys = __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e);
+        r[i] = __builtin_bit_cast(
+            Vec, __builtin_amdgcn_raw_buffer_load_b64(rsrc, lane_off, first * D * ESZ, 0));
+        int phys = block_id(j, i);
         phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;
         sc[i] = scales[(size_t)phys * p.num_kv_heads + kvh];
+      } else {
+        r[i] = __builtin_bit_cast(
+            Vec, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, first * D * ESZ, 0));
       }
-    }
-    if constexpr (!FP8) {
-      const int t0 = chunk_start(j);
-      if (app >= t0 && app < t0 + CT) nr = *reinterpret_cast<const Vec*>(nbase + new_off);
     }
   };
 
-  Vec kr[NI], vr[NI], kn, vn;
+  Vec kr[NI], vr[NI];
   float ks[NI], vs[NI];
-  float s[NI][G];
-  const char* knew = reinterpret_cast<const char*>(p.k_new);
-  const char* vnew = reinterpret_cast<const char*>(p.v_new);
 
-  // Rotating pipeline: K(j+1) is issued right after the scores of chunk j, V(j+1)
-  // right after its value sums, so the next chunk's loads fly during compute with
-  // no extra registers.
-  if (my_n > 0) {
-    issue(0, kbase, knew, kr, kn, ks, p.k_scale, true);
-    issue(0, vbase, vnew, vr, vn, vs, p.v_scale, false);
-  }
-  for (int j = 0; j < my_n; ++j) {
+  // One chunk: partial dot products -> LDS; each lane sums and exponentiates its
+  // own (token, head) scores; weights -> LDS; value sums.  SLOW handles the
+  // split's tail chunk (rows past the end); the fast path has no per-row selects.
+  auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;     // chunk j+1 exists
     const int t0 = chunk_start(j);
-    const bool masked = t0 + CT > s1;
-    const bool has_app = app >= t0 && app < t0 + CT;           // uniform
-    const int i_app = (app - t0) / TPI;
-    const bool row_app = has_app && (app - t0) % TPI == row;
-    // scores (base-2 units)
+    const int nvalid = s1 - t0;                      // rows t < nvalid are real
+    if constexpr (SLOW) {
+      // zero V rows past the split end (their slots may hold NaN poison)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (i * TPI + row >= nvalid) vr[i] = Vec{};
+    }
+    // partial dot products of this lane's 8 dims, per head
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      Vec kk = kr[i];
-      if (has_app && i == i_app && row_app) kk = kn;
+      const Vec kk = kr[i];
       float part[G];
       if constexpr (FP8) {
         float kf[8];
@@ -354,7 +442,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
           float a = 0.f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) a = fmaf(qf[g][k], kf[k], a);
-          part[g] = a;
+          part[g] = a * ks[i];
         }
       } else {
 #pragma unroll
@@ -365,94 +453,140 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
           part[g] = dot2_bf16(qw[g][3], kk.w, a);
         }
       }
-      const float sc = FP8 ? p.scale_log2 * ks[i] : p.scale_log2;
-      const bool valid = !masked || (t0 + i * TPI + row < s1);
+      float* dst = sm_part + (i * TPI + row) * PSTR + col;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float tot = row_sum<LPT>(part[g]) * sc;
-        s[i][g] = valid ? tot : kNegInf;
-      }
+      for (int g = 0; g < G; ++g) dst[g * GSTR] = part[g];
     }
-    if (j + 1 < my_n) {
+    __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
+    if constexpr (NEXT) {
       if (j + 1 - j0 >= CPG) {
         j0 += CPG;
-        ids = load_ids(j0);
+        ids = load_ids(s0, s1, my_n, j0);
       }
-      issue(j + 1, kbase, knew, kr, kn, ks, p.k_scale, true);
+      issue(j + 1, kbase, kr, ks, p.k_scale, true);
     }
-    // online softmax per row stream, lazy reference max
+    __builtin_amdgcn_wave_barrier();
+    // this lane's scores: token t = lane / G + q * TSTEP, head sg
+    float sc[PPL];
+    float cmax = kNegInf;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float cmax = s[0][g];
+    for (int q = 0; q < PPL; ++q) {
+      const int t = lane / G + q * TSTEP;
+      float tot = kNegInf;
+      if (t < CT) {
+        const float4* src = reinterpret_cast<const float4*>(sm_part + t * PSTR + sg * GSTR);
+        float a = 0.f;
 #pragma unroll
-      for (int i = 1; i < NI; ++i) cmax = fmaxf(cmax, s[i][g]);
-      if (cmax > m[g] + kLazyLog2) {
-        const float alpha = fast_exp2(m[g] - cmax);     // 0 while m = -inf
-        l[g] *= alpha;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
-        m[g] = cmax;
+        for (int c4 = 0; c4 < LPT / 4; ++c4) {
+          const float4 v = src[c4];
+          a += (v.x + v.y) + (v.z + v.w);
+        }
+        tot = a * p.scale_log2;
+        if (SLOW && t >= nvalid) tot = kNegInf;
       }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        // masked rows may still have m = -inf: select, do not subtract
-        const float pw = (!masked || s[i][g] > kNegInf) ? fast_exp2(s[i][g] - m[g]) : 0.f;
-        s[i][g] = pw;
-        l[g] += pw;
-      }
+      sc[q] = tot;
+      cmax = fmaxf(cmax, tot);
     }
-    // value sums; masked rows may hold NaN-poisoned slots: zero them
+    cmax = class_max<G>(cmax);                     // chunk max of head sg, wave-wide
+    // lazy rescale: only when the chunk max passes the reference by 2^kLazyLog2
+    const bool need = cmax > m_ref + kLazyLog2;
+    const bool any_need = __any(need);
+    if (any_need) {
+      const float m_new = need ? cmax : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);   // 0 while m_ref = -inf; 1 if kept
+      l_part *= alpha;
+      m_ref = m_new;
+      if (lane < G) sm_alpha[lane] = alpha;
+    }
+#pragma unroll
+    for (int q = 0; q < PPL; ++q) {
+      const int t = lane / G + q * TSTEP;
+      const float pw = (!SLOW || sc[q] > kNegInf) ? fast_exp2(sc[q] - m_ref) : 0.f;
+      l_part += (t < CT) ? pw : 0.f;
+      if (t < CT) sm_pw[t * G + sg] = pw;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (any_need) {
+      float al[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) al[g] = sm_alpha[g];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[g][k] *= al[g];
+    }
+    // value sums
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      Vec vv = vr[i];
-      if (has_app && i == i_app && row_app) vv = vn;
       float vf[8];
-      widen8<FP8>(vv, vf);
-      if (masked && t0 + i * TPI + row >= s1) {
+      widen8<FP8>(vr[i], vf);
+      float pw[G];
+      const float* src = sm_pw + (i * TPI + row) * G;
+      if constexpr (G % 4 == 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) vf[k] = 0.f;
+        for (int g4 = 0; g4 < G / 4; ++g4) {
+          const float4 v = reinterpret_cast<const float4*>(src)[g4];
+          pw[4 * g4] = v.x; pw[4 * g4 + 1] = v.y; pw[4 * g4 + 2] = v.z; pw[4 * g4 + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) pw[g] = src[g];
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float pg = FP8 ? s[i][g] * vs[i] : s[i][g];
+        const float pg = FP8 ? pw[g] * vs[i] : pw[g];
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pg, vf[k], acc[g][k]);
       }
     }
-    if (j + 1 < my_n) issue(j + 1, vbase, vnew, vr, vn, vs, p.v_scale, false);
+    __builtin_amdgcn_sched_barrier(0);   // keep V(j+1) behind the value sums of chunk j
+    if constexpr (NEXT) issue(j + 1, vbase, vr, vs, p.v_scale, false);
+  };
+
+  // Rotating pipeline: K(j+1) is issued right after the partial scores of chunk
+  // j, V(j+1) right after its value sums, so the next chunk's loads fly during
+  // compute with no extra registers.
+  if (my_n > 0) {
+    issue(0, kbase, kr, ks, p.k_scale, true);
+    issue(0, vbase, vr, vs, p.v_scale, false);
+  }
+  // Only a wave's last chunk can be partial, so the loop runs the fast path
+  // only, and the last chunk is peeled, which also lets every loop iteration
+  // issue the next loads unconditionally (K/V registers are reused in place).
+  for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
+  if (my_n > 0) {
+    const int t0 = chunk_start(my_n - 1);
+    if (t0 + CT > s1)
+      run_chunk(my_n - 1, std::true_type{}, std::false_type{});
+    else
+      run_chunk(my_n - 1, std::false_type{}, std::false_type{});
   }
 
-  // Merge the TPI row streams of the wave (row r holds lanes r*LPT ..).
+  // Wave result: rows share m_ref, so value sums add without rescaling; l adds
+  // over the lanes holding the same head.
 #pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mp = __shfl_xor(m[g], off, kWave);
-      const float lp = __shfl_xor(l[g], off, kWave);
-      const float M = fmaxf(m[g], mp);
-      const float a = m[g] > kNegInf ? fast_exp2(m[g] - M) : 0.f;
-      const float c = mp > kNegInf ? fast_exp2(mp - M) : 0.f;
-      l[g] = a * l[g] + c * lp;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[g][k] = a * acc[g][k] + c * __shfl_xor(acc[g][k], off, kWave);
-      m[g] = M;
+    for (int k = 0; k < 8; ++k) {
+      float x = acc[g][k];
+      if constexpr (LPT == 8) x += ror<8>(x);
+      x = sum_swap16(x);
+      acc[g][k] = sum_swap32(x);
     }
-  }
+  const float l_wave = class_sum<G>(l_part);      // lanes l = g (mod G) hold head g
   const bool wave_bad = __any(bad);
+  __syncthreads();                                 // transpose area becomes sm_acc
   if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int k = 0; k < 8; ++k) sm_acc(wave, g, col * 8 + k) = acc[g][k];
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sm_m[wave][g] = m[g];
-      sm_l[wave][g] = l[g];
-    }
-    sm_flag[wave] = wave_bad ? 1 : 0;
+  if (lane < G) {
+    sm_m[wave][lane] = m_ref;
+    sm_l[wave][lane] = l_wave;
   }
+  if (lane == 0) sm_flag[wave] = wave_bad ? 1 : 0;
   __syncthreads();
 
   // Merge the waves: this split's normalised output and base-2 lse.

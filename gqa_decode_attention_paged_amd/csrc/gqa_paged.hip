@@ -228,6 +228,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   p.num_blocks = s->num_blocks;
   p.max_blocks = s->max_blocks_per_seq;
   p.max_splits = max_splits;
+  p.hint_ctx = max_context_len;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
