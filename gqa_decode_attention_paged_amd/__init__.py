@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_page
 
 GQA_KV_BF16 = 0
 GQA_KV_FP8_E4M3 = 1
+GQA_FLAG_BATCH_INVARIANT = 1
 STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
                 3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
 
@@ -38,7 +39,8 @@ class PagedShape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+                ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class GqaError(RuntimeError):
@@ -117,10 +119,10 @@ def _kv_dtype(cache) -> int:
     raise TypeError(f"unsupported KV cache dtype {cache.dtype}")
 
 
-def make_shape(num_seqs, num_q_heads, k_cache, block_tables) -> PagedShape:
+def make_shape(num_seqs, num_q_heads, k_cache, block_tables, batch_invariant=False) -> PagedShape:
     nb, hkv, bs, d = k_cache.shape
     return PagedShape(num_seqs, num_q_heads, hkv, d, bs, nb, block_tables.shape[1],
-                      _kv_dtype(k_cache))
+                      _kv_dtype(k_cache), GQA_FLAG_BATCH_INVARIANT if batch_invariant else 0)
 
 
 def num_splits(context_len: int) -> int:
@@ -143,12 +145,12 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions):
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                            softmax_scale=None, k_scale=None, v_scale=None, out=None,
-                           out_lse=None, workspace=None, return_lse=True):
+                           out_lse=None, workspace=None, return_lse=True, batch_invariant=False):
     """Decode attention for a batch; returns (out, lse) (lse None if not requested)."""
     import torch
     lib = load()
     B, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -174,12 +176,13 @@ def make_workspace(shape: PagedShape, max_context_len: int, device):
 
 def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, block_tables,
                                   context_lens, max_context_len, softmax_scale=None, out=None,
-                                  out_lse=None, workspace=None, return_lse=True):
+                                  out_lse=None, workspace=None, return_lse=True,
+                                  batch_invariant=False):
     """Fused decode step: commit the new token at positions[b], then attend (one kernel)."""
     import torch
     lib = load()
     B, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -209,7 +212,7 @@ def kv_gather(cache, block_tables, seq, num_tokens):
     lib = load()
     nb, hkv, bs, d = cache.shape
     shape = PagedShape(block_tables.shape[0], hkv, hkv, d, bs, nb, block_tables.shape[1],
-                       _kv_dtype(cache))
+                       _kv_dtype(cache), 0)
     out = torch.empty((hkv, num_tokens, d), dtype=cache.dtype, device=cache.device)
     _check(lib.gqa_kv_gather(ctypes.byref(shape), _ptr(cache), _ptr(block_tables), int(seq),
                              int(num_tokens), _ptr(out), _stream(cache)))

@@ -8,14 +8,16 @@ namespace gqa {
 
 constexpr int kWave = 64;
 
-// Split policy.  A sequence of ctx tokens is cut into at most kMaxSplits
+// Split policy.  A sequence of ctx tokens is cut into at most `target`
 // contiguous token ranges ("splits") of split_tokens tokens each (a multiple of
 // kChunkTokens, so every split starts on a block boundary for block sizes 16
-// and 32).  Each split becomes one workgroup per KV head; its partial result
-// is merged by the log-sum-exp reduce.  The plan depends on ctx alone, never
-// on the batch, so a sequence's result is the same bits whatever it is batched
-// with.
-constexpr int kMaxSplits = 64;        // also the reduce kernel's lanes
+// and 32), and no split is shorter than kMinSplitTokens unless the whole
+// context is.  Each split becomes one workgroup per KV head; the splits of a
+// (sequence, KV head) are merged by log-sum-exp.  The host picks `target`:
+// either from the GPU's resident-workgroup capacity and the batch's number of
+// (sequence, KV head) pairs, or kMaxSplits when results must not depend on the
+// rest of the batch.
+constexpr int kMaxSplits = 64;        // also the final merge's lanes per head
 constexpr int kMinSplitTokens = 128;
 constexpr int kChunkTokens = 32;      // tokens one wave handles per iteration
 
@@ -24,10 +26,11 @@ struct SplitPlan {
   int split_tokens;
 };
 
-__host__ __device__ inline SplitPlan split_plan(int ctx) {
+__host__ __device__ inline SplitPlan split_plan(int ctx, int target = kMaxSplits) {
   if (ctx <= 0) return {0, 0};
   int n = (ctx + kMinSplitTokens - 1) / kMinSplitTokens;
-  if (n > kMaxSplits) n = kMaxSplits;
+  if (n > target) n = target;
+  if (n < 1) n = 1;
   int st = (ctx + n - 1) / n;
   st = (st + kChunkTokens - 1) / kChunkTokens * kChunkTokens;
   return {(ctx + st - 1) / st, st};

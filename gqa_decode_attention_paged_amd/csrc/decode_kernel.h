@@ -69,10 +69,12 @@ struct DecodeParams {
   int32_t max_blocks;
   int32_t max_splits;
   int32_t hint_ctx;             // host bound on context lengths (sizes the grid)
+  int32_t target_splits;        // split-count target of the split plan
   float scale_log2;             // softmax_scale * log2(e)
 };
 
 constexpr float kLazyLog2 = 8.0f;
+constexpr int kMergeBatch = 16;     // partial loads in flight per thread in the final merge
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int CTRL>
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     const int nch = (s1_ - s0_ + CT - 1) / CT;
     return wave < nch ? (nch - wave + WAVES - 1) / WAVES : 0;
   };
-  const SplitPlan hplan = split_plan(p.hint_ctx);
+  const SplitPlan hplan = split_plan(p.hint_ctx, p.target_splits);
   const int hs0 = split * hplan.split_tokens;
   const int hs1 = min(p.hint_ctx, hs0 + hplan.split_tokens);
   const int hmy_n = split < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
 
   const int ctx = p.context_lens[b];
   const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS;
-  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx);
+  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx, p.target_splits);
   const bool too_long = plan.num_splits > p.max_splits;
   const int pos = p.positions ? p.positions[b] : -1;
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
@@ -631,6 +633,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   __syncthreads();
   if (!sm_flag[WAVES]) return;
 
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_o + prow * G * D, 0, nsplit * G * D * 4, kBufferRsrcWord3);
   // Split weights per head: w_s = 2^(lse_s - M) / sum, one wave per head.
   float* sm_w = sm_buf;                            // [G][64]
   float* sm_lse = sm_buf + G * kWave;              // [G] merged base-2 lse
@@ -647,31 +651,30 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   __syncthreads();
 
   // out[g][d] = sum_s w_s o_s[g][d] over float4 columns; SP threads share a
-  // column (splits part, part + SP, ...) and combine through LDS.
+  // column (splits part, part + SP, ...) and combine through LDS.  The partial
+  // loads do not depend on the weights, so each batch of kMergeBatch loads is
+  // issued before the weights are needed.
   float4* outp = reinterpret_cast<float4*>(p.out + ((size_t)b * p.num_q_heads + h0) * D);
-  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-      p.ws_o + prow * G * D, 0, nsplit * G * D * 4, kBufferRsrcWord3);
   const int part = NT >= C4 ? tid / C4 : 0;
   for (int c = NT >= C4 ? tid % C4 : tid; c < C4; c += NT >= C4 ? C4 : NT) {
     const int g = (c * 4) / D;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sb = part; sb < nsplit; sb += 8 * SP) {
-      float4 v[8];
-      float w[8];
+    for (int sb = part; sb < nsplit; sb += kMergeBatch * SP) {
+      f32x4 v[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kMergeBatch; ++u) {
         const int si = sb + u * SP;
-        const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-            src, (si < nsplit ? si * C4 + c : 0) * 16, 0, kCachePolicySc1);
-        v[u] = si < nsplit ? make_float4(x.x, x.y, x.z, x.w) : make_float4(0.f, 0.f, 0.f, 0.f);
-        w[u] = si < nsplit ? sm_w[g * kWave + si] : 0.f;
+        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   src, (si < nsplit ? si * C4 + c : 0) * 16, 0, kCachePolicySc1));
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        o.x = fmaf(w[u], v[u].x, o.x);
-        o.y = fmaf(w[u], v[u].y, o.y);
-        o.z = fmaf(w[u], v[u].z, o.z);
-        o.w = fmaf(w[u], v[u].w, o.w);
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int si = sb + u * SP;
+        const float w = si < nsplit ? sm_w[g * kWave + si] : 0.f;
+        o.x = fmaf(w, v[u].x, o.x);
+        o.y = fmaf(w, v[u].y, o.y);
+        o.z = fmaf(w, v[u].z, o.z);
+        o.w = fmaf(w, v[u].w, o.w);
       }
     }
     if constexpr (SP > 1) sm_red[part * C4 + c] = o;

@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "gqa_paged.h"
 #include "common.h"
@@ -60,6 +63,8 @@ gqa_status check_shape(const gqa_paged_shape* s) {
     return fail(GQA_ERR_UNSUPPORTED, "block_size=%d not in {16,32}", s->block_size);
   if (s->kv_dtype != GQA_KV_BF16 && s->kv_dtype != GQA_KV_FP8_E4M3)
     return fail(GQA_ERR_UNSUPPORTED, "kv_dtype=%d unknown", s->kv_dtype);
+  if (s->flags & ~GQA_FLAG_BATCH_INVARIANT)
+    return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)s->flags);
   if ((int64_t)s->max_blocks_per_seq * s->block_size > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size overflows int32");
   return GQA_OK;
@@ -108,6 +113,41 @@ const void* pick_kernel_bs(int G, bool fp8) {
 const void* pick_kernel(int D, int BS, int G, bool fp8) {
   if (D == 64) return BS == 16 ? pick_kernel_bs<64, 16>(G, fp8) : pick_kernel_bs<64, 32>(G, fp8);
   return BS == 16 ? pick_kernel_bs<128, 16>(G, fp8) : pick_kernel_bs<128, 32>(G, fp8);
+}
+
+// Workgroups of `fn` the current device keeps resident at once (compute units
+// times workgroups per unit at this kernel's register and LDS use); cached.
+int resident_workgroups(const void* fn, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, fn});
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
+    return 0;
+  const int cap = cus * (per_cu > 0 ? per_cu : 1);
+  cache[{dev, fn}] = cap;
+  return cap;
+}
+
+// Split-count target.  By default, enough splits that the batch's (sequence,
+// KV head) pairs fill the resident-workgroup capacity once (fewer, longer
+// splits amortise each workgroup's start-up and merge).  With
+// GQA_FLAG_BATCH_INVARIANT, the fixed maximum, so the split of a sequence
+// depends on its own length only.
+int target_splits(const gqa_paged_shape* s, const void* fn, int threads) {
+  if (s->flags & GQA_FLAG_BATCH_INVARIANT) return gqa::kMaxSplits;
+  const int cap = resident_workgroups(fn, threads);
+  if (cap <= 0) return gqa::kMaxSplits;
+  const int64_t pairs = (int64_t)s->num_seqs * s->num_kv_heads;
+  int64_t t = (cap + pairs - 1) / pairs;
+  if (t < 1) t = 1;
+  if (t > gqa::kMaxSplits) t = gqa::kMaxSplits;
+  return (int)t;
 }
 
 gqa_status launch(const void* fn, dim3 grid, dim3 block, void* params, const char* what,
@@ -195,17 +235,21 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
     return fail(GQA_ERR_INVALID_ARG, "decode: q, caches, new rows and out must be 16-byte aligned");
-  const int max_splits = max_splits_for(max_context_len);
-  const WorkspaceLayout wl = workspace_layout(s, max_splits);
+  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len));
   if (!workspace || workspace_bytes < wl.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 wl.total);
   if (!aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8);
+  if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
+  const int target = target_splits(s, fn, kWaves * 64);
+  int max_splits = gqa::split_plan(max_context_len, target).num_splits;
+  if (max_splits < 1) max_splits = 1;
   if ((int64_t)max_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "grid too large");
 
-  const int G = s->num_q_heads / s->num_kv_heads;
   char* ws = static_cast<char*>(workspace);
   gqa::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -229,9 +273,8 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   p.max_blocks = s->max_blocks_per_seq;
   p.max_splits = max_splits;
   p.hint_ctx = max_context_len;
+  p.target_splits = target;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8);
-  if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
   st = launch(fn, dim3(max_splits, s->num_kv_heads, s->num_seqs), dim3(kWaves * 64), &p,
               "paged_decode", stream);
   return st == GQA_OK ? ok() : st;

@@ -72,6 +72,17 @@ typedef enum gqa_kv_dtype {
   GQA_KV_FP8_E4M3 = 1
 } gqa_kv_dtype;
 
+/* Shape flags. */
+enum {
+  /* Split every sequence's context by its own length only (the split plan of
+   * gqa_decode_num_splits), so a sequence's attention result is bit-identical
+   * whatever else is in the batch.  Without it the split count also follows
+   * the batch size (more, shorter splits when the batch is small), which is
+   * faster but makes results depend on the batch size in the last bits; they
+   * never depend on the order of the sequences. */
+  GQA_FLAG_BATCH_INVARIANT = 1
+};
+
 /* Host-side description of one paged KV cache and one batch of sequences. */
 typedef struct gqa_paged_shape {
   int32_t num_seqs;            /* B: sequences in the batch (0 is a no-op)           */
@@ -82,6 +93,7 @@ typedef struct gqa_paged_shape {
   int32_t num_blocks;          /* physical blocks in each pool                        */
   int32_t max_blocks_per_seq;  /* row length of block_tables                          */
   int32_t kv_dtype;            /* gqa_kv_dtype                                        */
+  int32_t flags;               /* GQA_FLAG_* bits (0 = default)                      */
 } gqa_paged_shape;
 
 /*
@@ -103,10 +115,10 @@ gqa_status gqa_kv_append(const gqa_paged_shape* shape,
                          hipStream_t stream);
 
 /*
- * gqa_decode_num_splits — the context split policy (host function, no GPU).
- * Returns how many partial attentions a sequence of `context_len` tokens is cut
- * into.  It depends on that sequence's own length only, so a sequence's result
- * does not depend on the rest of the batch.  0 for context_len <= 0.
+ * gqa_decode_num_splits — the batch-invariant context split plan (host
+ * function, no GPU): how many partial attentions a sequence of `context_len`
+ * tokens is cut into under GQA_FLAG_BATCH_INVARIANT, which is also the most
+ * any plan uses.  0 for context_len <= 0.
  */
 int32_t gqa_decode_num_splits(int32_t context_len);
 

@@ -41,7 +41,7 @@ def to_device(case, device="cuda:0"):
     return d
 
 
-def run_step(gqa, dev, case, max_context_len=None):
+def run_step(gqa, dev, case, max_context_len=None, batch_invariant=False):
     """One decode step through the C ABI: append (if the workload has one), then attention."""
     import torch
     if case["k_new"] is not None:
@@ -52,7 +52,8 @@ def run_step(gqa, dev, case, max_context_len=None):
     out, lse = gqa.paged_decode_attention(dev["q"], dev["k_cache"], dev["v_cache"],
                                           dev["block_tables"], dev["context_lens"],
                                           max_context_len, case["softmax_scale"],
-                                          dev["k_scale"], dev["v_scale"])
+                                          dev["k_scale"], dev["v_scale"],
+                                          batch_invariant=batch_invariant)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

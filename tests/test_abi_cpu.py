@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 def _shape(**kw):
     from gqa_decode_attention_paged_amd import PagedShape
     base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
-                num_blocks=1024, max_blocks_per_seq=600, kv_dtype=0)
+                num_blocks=1024, max_blocks_per_seq=600, kv_dtype=0, flags=0)
     base.update(kw)
     return PagedShape(**base)
 
@@ -87,7 +87,7 @@ def _call_decode(lib, shape, ws_bytes=1 << 30, ptr=16, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(head_dim=96), 2), (dict(block_size=8), 2), (dict(num_q_heads=24), 2),
     (dict(num_q_heads=30), 1), (dict(num_seqs=-1), 1), (dict(kv_dtype=7), 2),
-    (dict(num_blocks=0), 1),
+    (dict(num_blocks=0), 1), (dict(flags=6), 1),
 ])
 def test_decode_rejects_bad_shapes(lib, over, status):
     assert _call_decode(lib, _shape(**over)) == status

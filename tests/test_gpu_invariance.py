@@ -28,26 +28,46 @@ def test_block_permutation_is_bit_identical(gpu):
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
-def test_batch_invariance_bitwise(gpu):
-    """A sequence gives the same bits alone, in a batch, and at another batch index."""
+def _batch_case():
     spec = small_spec(num_seqs=6, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                       context=("uniform", 1, 9000), case_id=4001)
-    case = make_case(spec, seed=2)
+    return make_case(spec, seed=2)
+
+
+def _one(case, b):
+    one = dict(case)
+    for key in ("q", "block_tables", "context_lens", "positions"):
+        one[key] = case[key][b:b + 1]
+    return one
+
+
+def test_batch_invariant_mode_bitwise(gpu):
+    """With the batch-invariant flag a sequence gives the same bits alone and in a
+    batch, whatever the launch hint."""
+    case = _batch_case()
     hint = case["block_tables"].shape[1] * 16          # the largest length the tables allow
-    out, lse = run_step(gpu, to_device(case), case, max_context_len=hint)
+    out, lse = run_step(gpu, to_device(case), case, max_context_len=hint, batch_invariant=True)
     for b in (0, 3, 5):
-        one = dict(case)
-        one["q"] = case["q"][b:b + 1]
-        one["block_tables"] = case["block_tables"][b:b + 1]
-        one["context_lens"] = case["context_lens"][b:b + 1]
-        one["positions"] = case["positions"][b:b + 1]
-        o1, l1 = run_step(gpu, to_device(one), one)          # smaller launch hint
+        one = _one(case, b)
+        o1, l1 = run_step(gpu, to_device(one), one, batch_invariant=True)   # smaller hint
         assert np.array_equal(o1[0], out[b]) and np.array_equal(l1[0], lse[b])
+
+
+def test_default_mode_order_invariant_and_batch_consistent(gpu):
+    """Default mode: reordering the batch changes no bit; a sequence alone agrees with
+    its batched result to fp32 rounding (the split count follows the batch size)."""
+    case = _batch_case()
+    hint = case["block_tables"].shape[1] * 16
+    out, lse = run_step(gpu, to_device(case), case, max_context_len=hint)
     rev = dict(case)
     for key in ("q", "block_tables", "context_lens", "positions"):
         rev[key] = np.ascontiguousarray(case[key][::-1])
     o2, l2 = run_step(gpu, to_device(rev), rev, max_context_len=hint)
     assert np.array_equal(o2[::-1], out) and np.array_equal(l2[::-1], lse)
+    for b in (0, 3, 5):
+        one = _one(case, b)
+        o1, l1 = run_step(gpu, to_device(one), one)
+        assert np.max(np.abs(o1[0] - out[b])) <= 1e-5 and np.max(np.abs(l1[0] - lse[b])) <= 1e-5
 
 
 def test_fp8_codes_decode_exactly(gpu):
