@@ -4,8 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
 
 One step = one pass of the decode hot path over one batch: the KV append of the
-new token (for workloads that append) followed by paged decode attention
-(split pass + log-sum-exp merge), all through the C ABI.  Inputs are seeded
+new token (for workloads that append) and paged decode attention, split over
+the context with the log-sum-exp merge done by each pair's last workgroup: one
+fused kernel launch through the C ABI.  Inputs are seeded
 synthetic tensors already resident in HBM when timing starts.  To measure HBM
 rather than the 256 MB on-die Infinity Cache, consecutive steps rotate over
 enough copies of the KV pool that each step's KV bytes were last touched at

@@ -633,8 +633,29 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   __syncthreads();
   if (!sm_flag[WAVES]) return;
 
+  // Final merge.  The partial outputs do not depend on the split weights, so
+  // the first batch of them is loaded before the weights are computed, and the
+  // weights' lse loads fly at the same time: one memory round trip.
   const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
       p.ws_o + prow * G * D, 0, nsplit * G * D * 4, kBufferRsrcWord3);
+  float4* outp = reinterpret_cast<float4*>(p.out + ((size_t)b * p.num_q_heads + h0) * D);
+  const int part = NT >= C4 ? tid / C4 : 0;        // this thread's splits: part, part + SP, ...
+  const int c0 = NT >= C4 ? tid % C4 : tid;        // first float4 column of this thread
+  // loads in flight per thread: enough for all splits when a column has many
+  // threads, else kMergeBatch per round
+  constexpr int MB = (kMaxSplits + SP - 1) / SP < kMergeBatch ? (kMaxSplits + SP - 1) / SP
+                                                                : kMergeBatch;
+  auto load_batch = [&](int c, int sb, f32x4 (&v)[MB]) {
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int si = sb + u * SP;
+      v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                 src, (si < nsplit ? si * C4 + c : 0) * 16, 0, kCachePolicySc1));
+    }
+  };
+  f32x4 v[MB];
+  if (c0 < C4) load_batch(c0, part, v);
+
   // Split weights per head: w_s = 2^(lse_s - M) / sum, one wave per head.
   float* sm_w = sm_buf;                            // [G][64]
   float* sm_lse = sm_buf + G * kWave;              // [G] merged base-2 lse
@@ -642,33 +663,22 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   for (int g = wave; g < G; g += WAVES) {
     const float x = lane < nsplit ? load_coherent(&p.ws_lse[(prow + lane) * G + g]) : kNegInf;
     const bool nan = __any(x != x);
-    const float M = wave_max(x);
+    const float M = class_max<1>(x);
     const float w = lane < nsplit ? fast_exp2(x - M) : 0.f;
-    const float L = wave_sum(w);
+    const float L = class_sum<1>(w);
     sm_w[g * kWave + lane] = nan ? __builtin_nanf("") : w / L;
     if (lane == 0) sm_lse[g] = nan ? __builtin_nanf("") : M + log2f(L);
   }
   __syncthreads();
 
   // out[g][d] = sum_s w_s o_s[g][d] over float4 columns; SP threads share a
-  // column (splits part, part + SP, ...) and combine through LDS.  The partial
-  // loads do not depend on the weights, so each batch of kMergeBatch loads is
-  // issued before the weights are needed.
-  float4* outp = reinterpret_cast<float4*>(p.out + ((size_t)b * p.num_q_heads + h0) * D);
-  const int part = NT >= C4 ? tid / C4 : 0;
-  for (int c = NT >= C4 ? tid % C4 : tid; c < C4; c += NT >= C4 ? C4 : NT) {
+  // column and combine through LDS.
+  for (int c = c0; c < C4; c += NT >= C4 ? C4 : NT) {
     const int g = (c * 4) / D;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sb = part; sb < nsplit; sb += kMergeBatch * SP) {
-      f32x4 v[kMergeBatch];
+    for (int sb = part;;) {
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int si = sb + u * SP;
-        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                   src, (si < nsplit ? si * C4 + c : 0) * 16, 0, kCachePolicySc1));
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
+      for (int u = 0; u < MB; ++u) {
         const int si = sb + u * SP;
         const float w = si < nsplit ? sm_w[g * kWave + si] : 0.f;
         o.x = fmaf(w, v[u].x, o.x);
@@ -676,9 +686,13 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         o.z = fmaf(w, v[u].z, o.z);
         o.w = fmaf(w, v[u].w, o.w);
       }
+      sb += MB * SP;
+      if (sb >= nsplit) break;
+      load_batch(c, sb, v);
     }
     if constexpr (SP > 1) sm_red[part * C4 + c] = o;
     else outp[c] = o;
+    if (c + (NT >= C4 ? C4 : NT) < C4) load_batch(c + (NT >= C4 ? C4 : NT), part, v);
   }
   if constexpr (SP > 1) {
     __syncthreads();
