@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 ROTATE_BYTES = 1 << 30         # distance between reuses of one pool copy
+COPY_BYTES = 256 << 20         # read and written by the PMC calibration kernel
 METRIC = "decode-attention KV-read HBM GB/s (% of MI355X peak) and µs/step"
 
 
@@ -65,6 +66,57 @@ def counted_traffic(workload):
     if t.get("kernel_source_sha") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_call")
+
+
+def _pmc_per_dispatch(run_dir, counter, name_filter):
+    """{dispatch id: counter value} for the dispatches of kernels whose name passes
+    name_filter, from a rocprofv3 `--pmc <counter> -f csv` output directory."""
+    import csv
+    import glob
+    vals, names = {}, {}
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter or not name_filter(row["Kernel_Name"]):
+                    continue
+                key = (path, row["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+                names[key] = row["Kernel_Name"]
+    return vals, names
+
+
+def write_traffic(workload, pmc_dir, kv_bytes):
+    """Turn four rocprofv3 PMC runs (decode FETCH_SIZE / WRITE_SIZE, calibration-copy
+    FETCH_SIZE / WRITE_SIZE, in <pmc_dir>/{fetch,write,copy_fetch,copy_write}) into
+    profiles/traffic_<workload>.json.  Counters are KiB per dispatch; each is scaled
+    by (known copy bytes) / (what the same counter reads for the copy kernel)."""
+    import statistics
+    is_decode = lambda n: "paged_decode_kernel" in n
+    is_copy = lambda n: "elementwise" in n and "Fill" not in n
+    out = {"workload": workload, "kernel_source_sha": kernel_source_hash(),
+           "algorithmic_bytes_per_call": kv_bytes}
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        cal, _ = _pmc_per_dispatch(os.path.join(pmc_dir, "copy_" + sub), counter, is_copy)
+        run, _ = _pmc_per_dispatch(os.path.join(pmc_dir, sub), counter, is_decode)
+        if not cal or not run:
+            raise SystemExit(f"{counter}: missing dispatches (copy {len(cal)}, decode {len(run)})")
+        cal_kib = statistics.median(cal.values())
+        scale = COPY_BYTES / (cal_kib * 1024.0)
+        kib = statistics.median(run.values())
+        out[counter] = {"decode_kib_median": kib, "decode_dispatches": len(run),
+                        "copy_kib_median": cal_kib, "copy_dispatches": len(cal),
+                        "scale": scale, "bytes_per_call": kib * 1024.0 * scale}
+    out["hbm_bytes_per_call"] = round(out["FETCH_SIZE"]["bytes_per_call"] +
+                                      out["WRITE_SIZE"]["bytes_per_call"])
+    out["traffic_over_algorithmic"] = out["hbm_bytes_per_call"] / kv_bytes
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(case, kv_bytes, min_seconds):
@@ -104,6 +156,9 @@ def main():
                     help="launch the timed steps eagerly instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (for scaling PMC byte counters)")
+    ap.add_argument("--traffic-from", metavar="PMC_DIR",
+                    help="host only: write profiles/traffic_<workload>.json from rocprofv3 "
+                         "PMC runs stored under PMC_DIR/{fetch,write,copy_fetch,copy_write}")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -112,18 +167,28 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    if args.traffic_from:
+        from workloads import make_case, SPECS
+        spec = SPECS[args.workload]
+        write_traffic(spec.name, args.traffic_from,
+                      kv_bytes_per_step(spec, make_case(spec, seed=args.seed)["context_lens"]))
+        return
+
     import torch
 
     import gqa_decode_attention_paged_amd as gqa
     from workloads import make_case, SPECS
 
     if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        # A plain elementwise kernel that reads and writes COPY_BYTES each: the known
+        # size against which the PMC byte counters are scaled.
+        src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": 256 << 20, "copies": 5}))
+        print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 5}))
         return
 
     gqa.load()
