@@ -62,7 +62,7 @@ struct DecodeParams {
   float* out_lse;               // [B][Hq] or null
   float* ws_o;                  // [B][Hkv][max_splits][G][D] partial outputs (normalised)
   float* ws_lse;                // [B][Hkv][max_splits][G]    partial base-2 lse
-  uint32_t* counters;           // [B][Hkv] arrivals; zero between calls
+  uint32_t* counters;           // [B][Hkv] arrivals, kCounterStride words apart; zero between calls
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t num_blocks;
@@ -74,6 +74,10 @@ struct DecodeParams {
 };
 
 constexpr float kLazyLog2 = 8.0f;
+// Arrival counters sit 256 B apart: the splits of every (sequence, KV head)
+// bump their counter at about the same moment, and counters sharing a cache
+// line would serialise all of those atomics.
+constexpr int kCounterStride = 64;
 constexpr int kMergeBatch = 16;     // partial loads in flight per thread in the final merge
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   wait_vector_memory();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[(size_t)b * p.num_kv_heads + kvh],
+    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[((size_t)b * p.num_kv_heads + kvh) * kCounterStride],
                                                  1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm_flag[WAVES] = prev == (uint32_t)(nsplit - 1);
   }
@@ -708,7 +712,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   }
   if (p.out_lse && tid < G) p.out_lse[(size_t)b * p.num_q_heads + h0 + tid] = sm_lse[tid] * kLn2;
   if (tid == 0)
-    __hip_atomic_store(&p.counters[(size_t)b * p.num_kv_heads + kvh], 0u, __ATOMIC_RELAXED,
+    __hip_atomic_store(&p.counters[((size_t)b * p.num_kv_heads + kvh) * kCounterStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 

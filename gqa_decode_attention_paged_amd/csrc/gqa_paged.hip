@@ -16,11 +16,11 @@
 #include "decode_kernel.h"
 #include "kv_cache_ops.h"
 
+
 namespace {
 
 thread_local std::string g_last_error;
 
-constexpr int kWaves = 4;
 
 gqa_status fail(gqa_status s, const char* fmt, ...) {
   char buf[512];
@@ -74,12 +74,13 @@ struct WorkspaceLayout {
   size_t o_off, lse_off, cnt_words, total;
 };
 
-// [counters: B*Hkv u32][partial outputs: B*Hkv*S*G*D fp32][partial lse: B*Hkv*S*G fp32]
-// The counters come first so that a workspace initialised for one shape serves
-// any later call with no more (sequence, KV head) pairs.
+// [counters: B*Hkv*kCounterStride u32][partial outputs: B*Hkv*S*G*D fp32]
+// [partial lse: B*Hkv*S*G fp32].  The counters come first so that a workspace
+// initialised for one shape serves any later call with no more (sequence, KV
+// head) pairs.
 WorkspaceLayout workspace_layout(const gqa_paged_shape* s, int max_splits) {
   WorkspaceLayout w;
-  w.cnt_words = (size_t)s->num_seqs * s->num_kv_heads;
+  w.cnt_words = (size_t)s->num_seqs * s->num_kv_heads * gqa::kCounterStride;
   const size_t rows = (size_t)s->num_seqs * s->num_q_heads * (size_t)max_splits;
   w.o_off = (w.cnt_words * sizeof(uint32_t) + 255) & ~size_t(255);
   w.lse_off = (w.o_off + rows * s->head_dim * sizeof(float) + 255) & ~size_t(255);
@@ -92,27 +93,42 @@ int max_splits_for(int32_t max_context_len) {
   return ms < 1 ? 1 : ms;
 }
 
-// Kernel dispatch over the supported (D, BS, G, dtype) combinations.
-template <int D, int BS, int G>
+// Kernel dispatch over the supported (D, BS, G, dtype, waves) combinations.
+template <int D, int BS, int G, int W>
 const void* pick_kernel_g(bool fp8) {
-  return fp8 ? reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, true, kWaves>)
-             : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, false, kWaves>);
+  return fp8 ? reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, true, W>)
+             : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, false, W>);
 }
 
-template <int D, int BS>
+template <int D, int BS, int W>
 const void* pick_kernel_bs(int G, bool fp8) {
   switch (G) {
-    case 1: return pick_kernel_g<D, BS, 1>(fp8);
-    case 2: return pick_kernel_g<D, BS, 2>(fp8);
-    case 4: return pick_kernel_g<D, BS, 4>(fp8);
-    case 8: return pick_kernel_g<D, BS, 8>(fp8);
+    case 1: return pick_kernel_g<D, BS, 1, W>(fp8);
+    case 2: return pick_kernel_g<D, BS, 2, W>(fp8);
+    case 4: return pick_kernel_g<D, BS, 4, W>(fp8);
+    case 8: return pick_kernel_g<D, BS, 8, W>(fp8);
   }
   return nullptr;
 }
 
-const void* pick_kernel(int D, int BS, int G, bool fp8) {
-  if (D == 64) return BS == 16 ? pick_kernel_bs<64, 16>(G, fp8) : pick_kernel_bs<64, 32>(G, fp8);
-  return BS == 16 ? pick_kernel_bs<128, 16>(G, fp8) : pick_kernel_bs<128, 32>(G, fp8);
+template <int W>
+const void* pick_kernel_w(int D, int BS, int G, bool fp8) {
+  if (D == 64)
+    return BS == 16 ? pick_kernel_bs<64, 16, W>(G, fp8) : pick_kernel_bs<64, 32, W>(G, fp8);
+  return BS == 16 ? pick_kernel_bs<128, 16, W>(G, fp8) : pick_kernel_bs<128, 32, W>(G, fp8);
+}
+
+const void* pick_kernel(int D, int BS, int G, bool fp8, int waves) {
+  return waves == 8 ? pick_kernel_w<8>(D, BS, G, fp8) : pick_kernel_w<4>(D, BS, G, fp8);
+}
+
+// Waves per workgroup.  An eight-wave workgroup covers twice the tokens of a
+// four-wave one at the same number of resident waves (one per CU instead of
+// two), so each (sequence, KV head) has half as many splits to publish, count
+// and merge.  Batch-invariant calls use four-wave workgroups over the fixed
+// 64-split plan, whose shortest splits (128 tokens) fill four waves.
+int pick_waves(const gqa_paged_shape* s) {
+  return (s->flags & GQA_FLAG_BATCH_INVARIANT) ? 4 : 8;
 }
 
 // Workgroups of `fn` the current device keeps resident at once (compute units
@@ -242,9 +258,10 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   if (!aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const int G = s->num_q_heads / s->num_kv_heads;
-  const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8);
+  const int waves = pick_waves(s);
+  const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
-  const int target = target_splits(s, fn, kWaves * 64);
+  const int target = target_splits(s, fn, waves * 64);
   int max_splits = gqa::split_plan(max_context_len, target).num_splits;
   if (max_splits < 1) max_splits = 1;
   if ((int64_t)max_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
@@ -275,7 +292,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   p.hint_ctx = max_context_len;
   p.target_splits = target;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  st = launch(fn, dim3(max_splits, s->num_kv_heads, s->num_seqs), dim3(kWaves * 64), &p,
+  st = launch(fn, dim3(max_splits, s->num_kv_heads, s->num_seqs), dim3(waves * 64), &p,
               "paged_decode", stream);
   return st == GQA_OK ? ok() : st;
 }

@@ -147,8 +147,9 @@ size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max
  *   workspace     device scratch of at least
  *                 gqa_paged_decode_workspace_size(shape, max_context_len) bytes,
  *                 16-byte aligned.  It starts with one arrival counter (u32) per
- *                 (sequence, KV head), followed by the partial results of the
- *                 context splits.  The first B*H_kv words must be zero before a
+ *                 (sequence, KV head), 256 bytes apart, followed by the partial
+ *                 results of the context splits.  The first B*H_kv*64 words
+ *                 (B*H_kv*256 bytes) must be zero before a
  *                 call (gqa_paged_decode_workspace_init, or any zero fill); every
  *                 call leaves them zero again, so a workspace prepared once serves
  *                 any later call with no more (sequence, KV head) pairs.  One
@@ -197,7 +198,7 @@ gqa_status gqa_paged_decode_append_attention(const gqa_paged_shape* shape,
 
 /*
  * gqa_paged_decode_workspace_init — zero the arrival counters (the first
- * B*H_kv words) of a workspace sized for (shape, max_context_len).  Enqueued on
+ * B*H_kv*64 words) of a workspace sized for (shape, max_context_len).  Enqueued on
  * `stream` as a small fill kernel (no memset), so it may be captured in a HIP
  * graph.
  */

@@ -66,7 +66,7 @@ def test_workspace_size_formula(lib):
     s = _shape()
     ms = gqa.num_splits(8192)
     rows = 2 * 32 * ms
-    o_off = (2 * 8 * 4 + 255) // 256 * 256          # counters come first
+    o_off = (2 * 8 * 64 * 4 + 255) // 256 * 256     # counters come first, 256 B apart
     lse_off = (o_off + rows * 128 * 4 + 255) // 256 * 256
     assert gqa.workspace_size(s, 8192) == lse_off + rows * 4
     assert gqa.workspace_size(_shape(head_dim=96), 8192) == 0      # unsupported
