@@ -25,16 +25,28 @@
 //    Mathematics of Transformer Inference* §11.
 //
 // gfx950 mapping.  A (block, KV head) tile is BS contiguous rows of D elements.
-// LPT = D/8 lanes cover one token row, 8 elements each (16 B bf16 / 8 B fp8), so
-// one wave load instruction reads TPI = 64/LPT whole rows, fully coalesced.
-// q for the G heads stays in registers (this lane's 8 dims).  A row's partial
-// dot products are summed across its lanes with DPP (xor 1, xor 2, half-row
-// mirror, row mirror), which leaves identical bits in every lane of the row.
-// Each of the TPI rows is its own online-softmax stream (tokens r, r+TPI, ...);
-// streams merge across the wave at the end, then across waves through LDS.
-// A wave walks its chunks (CT tokens) with the next chunk's loads in flight
-// while the current one is computed; the chunk's block ids come from one
-// vector load per wave, read out with readlane.
+// A wave walks its chunks of CT tokens with the next chunk's loads in flight
+// while the current one is computed; the chunk's block ids come from one vector
+// load per wave, read out with readlane, and every tile is read through a
+// buffer resource whose base is wave-uniform.  Two compute paths:
+//
+//  * Matrix path (bf16 pools, G >= 2).  Scores of a 16-token tile are one
+//    16x16x32 bf16 MFMA product per 32 dims, C[t][g] = K q^T: each lane loads
+//    16 B of one K row straight into the A-operand layout, q of the G heads is
+//    the B operand (columns >= G are zero).  The softmax runs in the product's
+//    output layout.  V rows are staged in LDS and read back with the gfx950
+//    transpose read, which hands each lane 4 consecutive tokens of one
+//    dimension: the B operand of C[g][d] += P V.  The weights P (fp32) enter as
+//    two bf16 operands, the rounded value and the rounded remainder, so the
+//    product carries them to about 16 significant bits; K, V and q are bf16
+//    already, so every product is exact and sums are fp32.
+//  * Vector path (fp8 pools, and G = 1 where 15 of 16 MFMA columns would idle).
+//    LPT = D/8 lanes cover one token row, 8 elements each (16 B bf16 / 8 B fp8),
+//    so one load instruction reads TPI = 64/LPT whole rows.  Partial dot
+//    products of each lane's 8 dims go through LDS so that every lane finishes
+//    whole (token, head) scores; value sums use fp32 FMAs on the widened rows.
+//
+// Waves merge through LDS, splits through the workspace (see above).
 //
 // The running max moves lazily: only when a chunk's max exceeds the reference
 // by more than 2^kLazyLog2 in weight, so weights stay <= 256; o/l and m + log2 l
@@ -208,27 +220,55 @@ __device__ __forceinline__ float class_sum(float x) {
   return sum_swap32(sum_swap16(x));
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// gfx950 LDS transpose read of 16-bit elements.  Within each 16-lane group, lane
+// 16q + 4r + c receives element c of the 8-byte pieces addressed by lanes
+// 16q + 4k + r, k = 0..3.  So when those lanes address row t0 + k, column n0 + 4r
+// of a row-major bf16 tile, this lane receives rows t0 .. t0+3 of column
+// n0 + 4r + c: four consecutive tokens of one dimension.
+__device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+}
+
 template <int D, int BS, int G, bool FP8, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParams p) {
-  constexpr int LPT = D / 8;                 // lanes per token row
-  constexpr int TPI = kWave / LPT;           // rows per load instruction
-  constexpr int CT = G >= 8 ? 16 : 32;       // tokens per wave chunk
-  constexpr int NI = CT / TPI;               // load instructions per chunk (each of K, V)
+  // bf16 groups of two or more query heads use the matrix path; fp8 pools and
+  // single-head groups the vector path.
+  constexpr bool MFMA = !FP8 && G >= 2;
+  constexpr int LPT = D / 8;                 // lanes per token row (8 elements each)
+  constexpr int TPI = kWave / LPT;           // rows per row-layout load instruction
+  constexpr int CT = (MFMA || G < 8) ? 32 : 16;   // tokens per wave chunk
+  constexpr int NI = CT / TPI;               // row-layout loads per chunk
   constexpr int EPC = CT >= BS ? CT / BS : 1;  // block-table entries per chunk
   constexpr int CPG = kWave / EPC;           // chunks per preloaded table group
   constexpr int ESZ = KVTraits<FP8>::kBytes;
   constexpr int NT = WAVES * kWave;
+  // Vector path.  LDS score transpose: partial dot products of token t, head g,
+  // lane column c at t*PSTR + g*GSTR + c; the weights p[t][g] at t*G + g.
   constexpr int NPAIR = CT * G;              // (token, head) scores per chunk
   constexpr int PPL = (NPAIR + kWave - 1) / kWave;   // scores per lane
   constexpr int TSTEP = kWave / G;           // token stride between a lane's scores
-  // LDS score transpose: partial dot products of token t, head g, lane column c
-  // at t*PSTR + g*GSTR + c; the weights p[t][g] at t*G + g.
   constexpr int GSTR = LPT + 4;
   constexpr int PSTR = G * GSTR + 4;
   constexpr int kPartFloats = CT * PSTR;
-  constexpr int kWaveFloats = kPartFloats + NPAIR + 4 * ((G + 3) / 4);
-  static_assert(BS % TPI == 0 && kChunkTokens % CT == 0, "tile geometry");
-  static_assert(kWave % G == 0 && PPL * TSTEP * G >= NPAIR, "score mapping");
+  constexpr int kValuWaveBytes = (kPartFloats + NPAIR + 4 * ((G + 3) / 4)) * 4;
+  // Matrix path: 16x16x32 bf16 MFMA tiles.  Staged V rows are VSTR elements
+  // apart (a shift of 8 banks per row for the transpose reads).
+  constexpr int KB = D / 32;                 // k-steps of the score product
+  constexpr int NK = 2 * KB;                 // K loads per chunk (two 16-token tiles)
+  constexpr int NN = D / 16;                 // n-tiles of the value product
+  constexpr int VSTR = D + 16;
+  constexpr int PRS = CT + 4;                // floats per staged weight row
+  constexpr int kMfmaWaveBytes = CT * VSTR * 2 + 16 * PRS * 4 + 16 * 4;
+  constexpr int kWaveBytes = MFMA ? kMfmaWaveBytes : kValuWaveBytes;
+  static_assert(BS % TPI == 0 && BS % 16 == 0 && kChunkTokens % CT == 0, "tile geometry");
+  static_assert(kWave % G == 0 && PPL * TSTEP * G >= NPAIR && G <= 16, "score mapping");
+  static_assert(kWaveBytes % 16 == 0, "LDS alignment");
   using Vec = typename KVTraits<FP8>::Vec;
 
   // Workgroup -> (split, KV head, sequence).  When the number of (sequence,
@@ -253,26 +293,25 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform per wave
-  const int row = lane / LPT;
-  const int col = lane % LPT;
+  const int row = lane / LPT;                // row layout: token row of this lane
+  const int col = lane % LPT;                // and its 8-element column
 
-  // LDS: per-wave score transpose during the chunk loop; afterwards (reused) the
+  // LDS: per-wave chunk staging during the loop; afterwards (reused) the
   // per-wave partial sums, then the split weights and float4 sums of the merge.
   constexpr int C4 = G * D / 4;                    // float4 columns of one head group
   constexpr int SP = NT >= C4 ? NT / C4 : 1;       // threads per column in the final merge
-  constexpr int kAccFloats = WAVES * G * D;
-  constexpr int kMergeFloats = G * kWave + 4 * ((G + 3) / 4) + 4 * SP * C4;
-  constexpr int kLoopFloats = WAVES * kWaveFloats;
-  constexpr int kBufA = kAccFloats > kMergeFloats ? kAccFloats : kMergeFloats;
-  constexpr int kBufFloats = kBufA > kLoopFloats ? kBufA : kLoopFloats;
-  __shared__ __attribute__((aligned(16))) float sm_buf[kBufFloats];
+  constexpr int kAccBytes = WAVES * G * D * 4;
+  constexpr int kMergeBytes = (G * kWave + 4 * ((G + 3) / 4) + 4 * SP * C4) * 4;
+  constexpr int kLoopBytes = WAVES * kWaveBytes;
+  constexpr int kBufA = kAccBytes > kMergeBytes ? kAccBytes : kMergeBytes;
+  constexpr int kBufBytes = kBufA > kLoopBytes ? kBufA : kLoopBytes;
+  __shared__ __attribute__((aligned(16))) char sm_raw[kBufBytes];
   __shared__ float sm_m[WAVES][G];
   __shared__ float sm_l[WAVES][G];
   __shared__ int sm_flag[WAVES + 1];
+  float* const sm_buf = reinterpret_cast<float*>(sm_raw);
   auto sm_acc = [&](int w, int g, int d) -> float& { return sm_buf[(w * G + g) * D + d]; };
-  float* sm_part = sm_buf + wave * kWaveFloats;    // this wave's transpose area
-  float* sm_pw = sm_part + kPartFloats;            // [CT][G] weights
-  float* sm_alpha = sm_pw + NPAIR;                 // [G] rescale factors
+  char* const sm_wave = sm_raw + wave * kWaveBytes;   // this wave's staging area
 
   // Speculative block-id prefetch: most batches have every sequence at the
   // launch hint's length, so the ids of this wave's chunks under the hint's
@@ -340,33 +379,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   }
   if (s0 != hs0 || s1 != hs1) ids = load_ids(s0, s1, my_n, 0);   // hint did not apply
 
-  // q: this lane's 8 dims of each of the G heads.
-  const uint16_t* qp = p.q + ((size_t)b * p.num_q_heads + h0) * D + col * 8;
-  uint32_t qw[G][4];
-  float qf[FP8 ? G : 1][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 v = *reinterpret_cast<const uint4*>(qp + (size_t)g * D);
-    qw[g][0] = v.x; qw[g][1] = v.y; qw[g][2] = v.z; qw[g][3] = v.w;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qf[g][2 * j] = bf16_lo(qw[g][j]);
-        qf[g][2 * j + 1] = bf16_hi(qw[g][j]);
-      }
-    }
-  }
-
-  // Online-softmax state.  The reference max m is wave-uniform per head (all
-  // rows share it), l is this lane's share of the exponential sum of its
-  // scores (head lane % G), acc the value sums of this lane's 8 dims.
-  const int sg = lane % G;                         // head of this lane's scores
+  // Online-softmax state shared by both paths: m_ref, the reference max of this
+  // lane's head (wave-uniform per head), and l_part, this lane's share of that
+  // head's exponential sum.
   float m_ref = kNegInf, l_part = 0.f;
-  float acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
   bool bad = false;
 
   const char* kbase = static_cast<const char*>(p.k_cache);
@@ -375,17 +391,12 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   const size_t block_stride = (size_t)p.num_kv_heads * kTileBytes;
   int j0 = 0;
 
-  // Instruction i of chunk j reads TPI rows of one (block, KV head) tile: a
-  // wave-uniform tile base (block id via readlane) plus this lane's 16 B slot.
-  const uint32_t lane_off = (uint32_t)lane * 8 * ESZ;
-  auto block_id = [&](int j, int i) {
-    const int e = CT >= BS ? (i * TPI) / BS : 0;
-    return __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e);
-  };
+  // Block id of table entry e of chunk j (wave-uniform, via readlane).
+  auto block_id = [&](int j, int e) { return __builtin_amdgcn_readlane(ids, (j - j0) * EPC + e); };
   // One (block, KV head) tile as a buffer resource: the block id is wave-uniform,
   // so the base lives in scalar registers and each lane adds its 32-bit offset.
-  auto tile_rsrc = [&](int j, int i, const char* pool, bool track) {
-    int phys = block_id(j, i);
+  auto tile_rsrc = [&](int j, int e, const char* pool, bool track) {
+    int phys = block_id(j, e);
     const bool ok = (unsigned)phys < (unsigned)p.num_blocks;
     if (track) bad |= !ok;
     phys = ok ? phys : 0;
@@ -394,21 +405,29 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         (int)kTileBytes, kBufferRsrcWord3);
   };
   auto chunk_start = [&](int j) { return s0 + (wave + j * WAVES) * CT; };
-
-  // Issue the loads of one tile (K or V) of chunk j.  Branch-free: every row
-  // reads an in-bounds slot (rows past the split end read their block's unused
-  // slots, whole groups past it read block 0) and compute masks them.
-  auto issue = [&](int j, const char* pool, Vec (&r)[NI], float (&sc)[NI],
-                   const float* scales, bool track) {
+  auto advance_ids = [&](int j) {        // before issuing chunk j + 1
+    if (j + 1 - j0 >= CPG) {
+      j0 += CPG;
+      ids = load_ids(s0, s1, my_n, j0);
+    }
+  };
+  // Row-layout loads of chunk j (V, and K on the vector path): instruction i
+  // reads TPI whole rows.  Branch-free: every row reads an in-bounds slot (rows
+  // past the split end read their block's unused slots, whole groups past it
+  // read block 0) and compute masks them.
+  const uint32_t lane_off = (uint32_t)lane * 8 * ESZ;
+  auto issue_rows = [&](int j, const char* pool, Vec (&r)[NI], float (&sc)[NI],
+                        const float* scales, bool track) {
     const int t0 = chunk_start(j);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const auto rsrc = tile_rsrc(j, i, pool, track);
+      const int e = CT >= BS ? (i * TPI) / BS : 0;
+      const auto rsrc = tile_rsrc(j, e, pool, track);
       const int first = (t0 + i * TPI) % BS;       // first row of this instruction, uniform
       if constexpr (FP8) {
         r[i] = __builtin_bit_cast(
             Vec, __builtin_amdgcn_raw_buffer_load_b64(rsrc, lane_off, first * D * ESZ, 0));
-        int phys = block_id(j, i);
+        int phys = block_id(j, e);
         phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;
         sc[i] = scales[(size_t)phys * p.num_kv_heads + kvh];
       } else {
@@ -418,179 +437,379 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     }
   };
 
-  Vec kr[NI], vr[NI];
-  float ks[NI], vs[NI];
+  bool wave_bad = false;
+  if constexpr (MFMA) {
+    // ---- Matrix path.  Scores C[t][g] = K q^T per 16-token tile (A = K rows,
+    // B = q), value sums C[g][d] += P V (A = weights, B = V read transposed from
+    // LDS).  Lane l is column hd = l & 15 and k-group qd = l >> 4 of each tile.
+    const int hd = lane & 15;
+    const int qd = lane >> 4;
+    uint16_t* sm_v = reinterpret_cast<uint16_t*>(sm_wave);            // [CT][VSTR] bf16
+    float* sm_pw = reinterpret_cast<float*>(sm_wave + CT * VSTR * 2);  // [16][PRS] weights
+    float* sm_alpha = sm_pw + 16 * PRS;                                // [16] rescale factors
 
-  // One chunk: partial dot products -> LDS; each lane sums and exponentiates its
-  // own (token, head) scores; weights -> LDS; value sums.  SLOW handles the
-  // split's tail chunk (rows past the end); the fast path has no per-row selects.
-  auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
-    constexpr bool SLOW = decltype(slow_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;     // chunk j+1 exists
-    const int t0 = chunk_start(j);
-    const int nvalid = s1 - t0;                      // rows t < nvalid are real
-    if constexpr (SLOW) {
-      // zero V rows past the split end (their slots may hold NaN poison)
+    bf16x8_t qop[KB];                     // q of head hd, dims 8*qd + 32*kb .. +7
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (i * TPI + row >= nvalid) vr[i] = Vec{};
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (hd < G)
+        v = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.num_q_heads + h0 + hd) * D +
+                                            8 * qd + 32 * kb);
+      qop[kb] = as_bf16x8(v);
     }
-    // partial dot products of this lane's 8 dims, per head
+    f32x4 acc[NN];                        // rows: heads 4*qd + r; columns: dims 16*n + hd
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const Vec kk = kr[i];
-      float part[G];
+    for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // K in the A-operand layout: row (lane & 15) of a 16-token tile, dims
+    // 8*qd + 32*kb .. +7 (each instruction reads 16 rows x 64 B).
+    const uint32_t k_lane_off = (uint32_t)((hd * D + 8 * qd) * 2);
+    uint4 kr[NK];
+    auto issue_k = [&](int j) {
+      const int t0 = chunk_start(j);
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) {
+        const int e = CT >= BS ? (16 * t16) / BS : 0;
+        const auto rsrc = tile_rsrc(j, e, kbase, true);
+        const int first = (t0 + 16 * t16) % BS;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kr[t16 * KB + kb] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_lane_off,
+                                                           (first * D + 32 * kb) * 2, 0));
+      }
+    };
+    Vec vr[NI];
+    float vs_unused[NI];
+    const int k4 = hd >> 2, r4 = lane & 3;   // transpose-read source row / column piece
+
+    auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
+      constexpr bool SLOW = decltype(slow_tag)::value;   // split tail: rows past s1
+      constexpr bool NEXT = decltype(next_tag)::value;   // chunk j+1 exists
+      const int t0 = chunk_start(j);
+      const int nvalid = s1 - t0;
+      f32x4 sc[2];
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) {
+        sc[t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          sc[t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t16 * KB + kb]),
+                                                           qop[kb], sc[t16], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the operands just used
+      if constexpr (NEXT) {
+        advance_ids(j);
+        issue_k(j + 1);
+      }
+      // This lane's scores: head hd, tokens 16*t16 + 4*qd + r.
+      float s[8];
+      float cmax = kNegInf;
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * t16 + 4 * qd + r;
+          float x = sc[t16][r] * p.scale_log2;
+          if (hd >= G || (SLOW && t >= nvalid)) x = kNegInf;
+          s[t16 * 4 + r] = x;
+          cmax = fmaxf(cmax, x);
+        }
+      cmax = max_swap32(max_swap16(cmax));   // chunk max of head hd, wave-wide
+      const bool need = cmax > m_ref + kLazyLog2;
+      const bool any_need = __any(need);
+      if (any_need) {
+        const float m_new = need ? cmax : m_ref;
+        const float alpha = m_new == m_ref ? 1.f : fast_exp2(m_ref - m_new);
+        l_part *= alpha;
+        m_ref = m_new;
+        if (lane < 16) sm_alpha[lane] = alpha;
+      }
+      float pw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pw[k] = s[k] > kNegInf ? fast_exp2(s[k] - m_ref) : 0.f;
+        l_part += pw[k];
+      }
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16)
+        *reinterpret_cast<float4*>(sm_pw + hd * PRS + 16 * t16 + 4 * qd) =
+            make_float4(pw[4 * t16], pw[4 * t16 + 1], pw[4 * t16 + 2], pw[4 * t16 + 3]);
+      // V rows to LDS (rows past the split end as zeros: their slots may hold
+      // NaN poison), then the next chunk's V loads reuse the registers.
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        Vec v = vr[i];
+        if (SLOW && i * TPI + row >= nvalid) v = Vec{};
+        *reinterpret_cast<Vec*>(sm_v + (i * TPI + row) * VSTR + 8 * col) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs_unused, nullptr, false);
+      __builtin_amdgcn_wave_barrier();
+      if (any_need) {
+        float al[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) al[r] = sm_alpha[4 * qd + r];
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[n][r] *= al[r];
+      }
+      // Weights as the A operand (head hd, tokens 8*qd .. +7), split into a bf16
+      // high part and the bf16 rounding of the remainder: two products give the
+      // weights to about 16 significant bits.
+      const float4 wa = *reinterpret_cast<const float4*>(sm_pw + hd * PRS + 8 * qd);
+      const float4 wb = *reinterpret_cast<const float4*>(sm_pw + hd * PRS + 8 * qd + 4);
+      const float wf[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      bf16x8_t whi, wlo;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        whi[k] = (__bf16)wf[k];
+        wlo[k] = (__bf16)(wf[k] - (float)whi[k]);
+      }
+      // Value sums: the B operand (tokens 8*qd .. +7 of dim 16*n + hd) comes from
+      // two transpose reads of the staged rows.
+#pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        const uint16_t* src = sm_v + (8 * qd + k4) * VSTR + 16 * n + 4 * r4;
+        const i16x4_t lo = lds_read_transposed(src);
+        const i16x4_t hi = lds_read_transposed(src + 4 * VSTR);
+        const bf16x8_t vop =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, vop, acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, vop, acc[n], 0, 0, 0);
+      }
+    };
+
+    // Rotating pipeline: K(j+1) is issued right after the scores of chunk j,
+    // V(j+1) as soon as V(j) is staged in LDS.
+    if (my_n > 0) {
+      issue_k(0);
+      issue_rows(0, vbase, vr, vs_unused, nullptr, false);
+    }
+    for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
+    if (my_n > 0) {
+      if (chunk_start(my_n - 1) + CT > s1)
+        run_chunk(my_n - 1, std::true_type{}, std::false_type{});
+      else
+        run_chunk(my_n - 1, std::false_type{}, std::false_type{});
+    }
+
+    // Wave result: the products already summed over tokens; l adds over the
+    // lanes of the same head (hd).
+    const float l_wave = sum_swap32(sum_swap16(l_part));
+    wave_bad = __any(bad);
+    __syncthreads();                                 // staging area becomes sm_acc
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * qd + r < G) sm_acc(wave, 4 * qd + r, 16 * n + hd) = acc[n][r];
+    if (lane < G) {
+      sm_m[wave][lane] = m_ref;
+      sm_l[wave][lane] = l_wave;
+    }
+  } else {
+    // ---- Vector path.  LPT lanes hold one token row (8 elements each); partial
+    // dot products go through LDS so each lane finishes whole scores.
+    float* sm_part = reinterpret_cast<float*>(sm_wave);   // transpose area
+    float* sm_pw = sm_part + kPartFloats;                 // [CT][G] weights
+    float* sm_alpha = sm_pw + NPAIR;                      // [G] rescale factors
+
+    // q: this lane's 8 dims of each of the G heads.
+    const uint16_t* qp = p.q + ((size_t)b * p.num_q_heads + h0) * D + col * 8;
+    uint32_t qw[G][4];
+    float qf[FP8 ? G : 1][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + (size_t)g * D);
+      qw[g][0] = v.x; qw[g][1] = v.y; qw[g][2] = v.z; qw[g][3] = v.w;
       if constexpr (FP8) {
-        float kf[8];
-        widen8<true>(kk, kf);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float a = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) a = fmaf(qf[g][k], kf[k], a);
-          part[g] = a * ks[i];
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float a = dot2_bf16(qw[g][0], kk.x, 0.f);
-          a = dot2_bf16(qw[g][1], kk.y, a);
-          a = dot2_bf16(qw[g][2], kk.z, a);
-          part[g] = dot2_bf16(qw[g][3], kk.w, a);
+        for (int j = 0; j < 4; ++j) {
+          qf[g][2 * j] = bf16_lo(qw[g][j]);
+          qf[g][2 * j + 1] = bf16_hi(qw[g][j]);
         }
       }
-      float* dst = sm_part + (i * TPI + row) * PSTR + col;
-#pragma unroll
-      for (int g = 0; g < G; ++g) dst[g * GSTR] = part[g];
     }
-    __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
-    if constexpr (NEXT) {
-      if (j + 1 - j0 >= CPG) {
-        j0 += CPG;
-        ids = load_ids(s0, s1, my_n, j0);
-      }
-      issue(j + 1, kbase, kr, ks, p.k_scale, true);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // this lane's scores: token t = lane / G + q * TSTEP, head sg
-    float sc[PPL];
-    float cmax = kNegInf;
-#pragma unroll
-    for (int q = 0; q < PPL; ++q) {
-      const int t = lane / G + q * TSTEP;
-      float tot = kNegInf;
-      if (t < CT) {
-        const float4* src = reinterpret_cast<const float4*>(sm_part + t * PSTR + sg * GSTR);
-        float a = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < LPT / 4; ++c4) {
-          const float4 v = src[c4];
-          a += (v.x + v.y) + (v.z + v.w);
-        }
-        tot = a * p.scale_log2;
-        if (SLOW && t >= nvalid) tot = kNegInf;
-      }
-      sc[q] = tot;
-      cmax = fmaxf(cmax, tot);
-    }
-    cmax = class_max<G>(cmax);                     // chunk max of head sg, wave-wide
-    // lazy rescale: only when the chunk max passes the reference by 2^kLazyLog2
-    const bool need = cmax > m_ref + kLazyLog2;
-    const bool any_need = __any(need);
-    if (any_need) {
-      const float m_new = need ? cmax : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);   // 0 while m_ref = -inf; 1 if kept
-      l_part *= alpha;
-      m_ref = m_new;
-      if (lane < G) sm_alpha[lane] = alpha;
-    }
-#pragma unroll
-    for (int q = 0; q < PPL; ++q) {
-      const int t = lane / G + q * TSTEP;
-      const float pw = (!SLOW || sc[q] > kNegInf) ? fast_exp2(sc[q] - m_ref) : 0.f;
-      l_part += (t < CT) ? pw : 0.f;
-      if (t < CT) sm_pw[t * G + sg] = pw;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (any_need) {
-      float al[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) al[g] = sm_alpha[g];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[g][k] *= al[g];
-    }
-    // value sums
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float vf[8];
-      widen8<FP8>(vr[i], vf);
-      float pw[G];
-      const float* src = sm_pw + (i * TPI + row) * G;
-      if constexpr (G % 4 == 0) {
-#pragma unroll
-        for (int g4 = 0; g4 < G / 4; ++g4) {
-          const float4 v = reinterpret_cast<const float4*>(src)[g4];
-          pw[4 * g4] = v.x; pw[4 * g4 + 1] = v.y; pw[4 * g4 + 2] = v.z; pw[4 * g4 + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) pw[g] = src[g];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pg = FP8 ? pw[g] * vs[i] : pw[g];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pg, vf[k], acc[g][k]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep V(j+1) behind the value sums of chunk j
-    if constexpr (NEXT) issue(j + 1, vbase, vr, vs, p.v_scale, false);
-  };
-
-  // Rotating pipeline: K(j+1) is issued right after the partial scores of chunk
-  // j, V(j+1) right after its value sums, so the next chunk's loads fly during
-  // compute with no extra registers.
-  if (my_n > 0) {
-    issue(0, kbase, kr, ks, p.k_scale, true);
-    issue(0, vbase, vr, vs, p.v_scale, false);
-  }
-  // Only a wave's last chunk can be partial, so the loop runs the fast path
-  // only, and the last chunk is peeled, which also lets every loop iteration
-  // issue the next loads unconditionally (K/V registers are reused in place).
-  for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
-  if (my_n > 0) {
-    const int t0 = chunk_start(my_n - 1);
-    if (t0 + CT > s1)
-      run_chunk(my_n - 1, std::true_type{}, std::false_type{});
-    else
-      run_chunk(my_n - 1, std::false_type{}, std::false_type{});
-  }
-
-  // Wave result: rows share m_ref, so value sums add without rescaling; l adds
-  // over the lanes holding the same head.
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float x = acc[g][k];
-      if constexpr (LPT == 8) x += ror<8>(x);
-      x = sum_swap16(x);
-      acc[g][k] = sum_swap32(x);
-    }
-  const float l_wave = class_sum<G>(l_part);      // lanes l = g (mod G) hold head g
-  const bool wave_bad = __any(bad);
-  __syncthreads();                                 // transpose area becomes sm_acc
-  if (row == 0) {
+    // This lane's scores are for head sg = lane % G; acc holds the value sums
+    // of this lane's 8 dims.
+    const int sg = lane % G;
+    float acc[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sm_acc(wave, g, col * 8 + k) = acc[g][k];
-  }
-  if (lane < G) {
-    sm_m[wave][lane] = m_ref;
-    sm_l[wave][lane] = l_wave;
+      for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
+    Vec kr[NI], vr[NI];
+    float ks[NI], vs[NI];
+
+    // One chunk: partial dot products -> LDS; each lane sums and exponentiates its
+    // own (token, head) scores; weights -> LDS; value sums.  SLOW handles the
+    // split's tail chunk (rows past the end); the fast path has no per-row selects.
+    auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
+      constexpr bool SLOW = decltype(slow_tag)::value;
+      constexpr bool NEXT = decltype(next_tag)::value;     // chunk j+1 exists
+      const int t0 = chunk_start(j);
+      const int nvalid = s1 - t0;                      // rows t < nvalid are real
+      if constexpr (SLOW) {
+        // zero V rows past the split end (their slots may hold NaN poison)
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          if (i * TPI + row >= nvalid) vr[i] = Vec{};
+      }
+      // partial dot products of this lane's 8 dims, per head
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const Vec kk = kr[i];
+        float part[G];
+        if constexpr (FP8) {
+          float kf[8];
+          widen8<true>(kk, kf);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a = fmaf(qf[g][k], kf[k], a);
+            part[g] = a * ks[i];
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float a = dot2_bf16(qw[g][0], kk.x, 0.f);
+            a = dot2_bf16(qw[g][1], kk.y, a);
+            a = dot2_bf16(qw[g][2], kk.z, a);
+            part[g] = dot2_bf16(qw[g][3], kk.w, a);
+          }
+        }
+        float* dst = sm_part + (i * TPI + row) * PSTR + col;
+#pragma unroll
+        for (int g = 0; g < G; ++g) dst[g * GSTR] = part[g];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
+      if constexpr (NEXT) {
+        advance_ids(j);
+        issue_rows(j + 1, kbase, kr, ks, p.k_scale, true);
+      }
+      __builtin_amdgcn_wave_barrier();
+      // this lane's scores: token t = lane / G + q * TSTEP, head sg
+      float sc[PPL];
+      float cmax = kNegInf;
+#pragma unroll
+      for (int q = 0; q < PPL; ++q) {
+        const int t = lane / G + q * TSTEP;
+        float tot = kNegInf;
+        if (t < CT) {
+          const float4* src = reinterpret_cast<const float4*>(sm_part + t * PSTR + sg * GSTR);
+          float a = 0.f;
+#pragma unroll
+          for (int c4 = 0; c4 < LPT / 4; ++c4) {
+            const float4 v = src[c4];
+            a += (v.x + v.y) + (v.z + v.w);
+          }
+          tot = a * p.scale_log2;
+          if (SLOW && t >= nvalid) tot = kNegInf;
+        }
+        sc[q] = tot;
+        cmax = fmaxf(cmax, tot);
+      }
+      cmax = class_max<G>(cmax);                     // chunk max of head sg, wave-wide
+      // lazy rescale: only when the chunk max passes the reference by 2^kLazyLog2
+      const bool need = cmax > m_ref + kLazyLog2;
+      const bool any_need = __any(need);
+      if (any_need) {
+        const float m_new = need ? cmax : m_ref;
+        const float alpha = fast_exp2(m_ref - m_new);   // 0 while m_ref = -inf; 1 if kept
+        l_part *= alpha;
+        m_ref = m_new;
+        if (lane < G) sm_alpha[lane] = alpha;
+      }
+#pragma unroll
+      for (int q = 0; q < PPL; ++q) {
+        const int t = lane / G + q * TSTEP;
+        const float pw = (!SLOW || sc[q] > kNegInf) ? fast_exp2(sc[q] - m_ref) : 0.f;
+        l_part += (t < CT) ? pw : 0.f;
+        if (t < CT) sm_pw[t * G + sg] = pw;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (any_need) {
+        float al[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) al[g] = sm_alpha[g];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[g][k] *= al[g];
+      }
+      // value sums
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float vf[8];
+        widen8<FP8>(vr[i], vf);
+        float pw[G];
+        const float* src = sm_pw + (i * TPI + row) * G;
+        if constexpr (G % 4 == 0) {
+#pragma unroll
+          for (int g4 = 0; g4 < G / 4; ++g4) {
+            const float4 v = reinterpret_cast<const float4*>(src)[g4];
+            pw[4 * g4] = v.x; pw[4 * g4 + 1] = v.y; pw[4 * g4 + 2] = v.z; pw[4 * g4 + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) pw[g] = src[g];
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pg = FP8 ? pw[g] * vs[i] : pw[g];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pg, vf[k], acc[g][k]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep V(j+1) behind the value sums of chunk j
+      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs, p.v_scale, false);
+    };
+
+    // Rotating pipeline: K(j+1) is issued right after the partial scores of chunk
+    // j, V(j+1) right after its value sums, so the next chunk's loads fly during
+    // compute with no extra registers.
+    if (my_n > 0) {
+      issue_rows(0, kbase, kr, ks, p.k_scale, true);
+      issue_rows(0, vbase, vr, vs, p.v_scale, false);
+    }
+    // Only a wave's last chunk can be partial, so the loop runs the fast path
+    // only, and the last chunk is peeled, which also lets every loop iteration
+    // issue the next loads unconditionally (K/V registers are reused in place).
+    for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
+    if (my_n > 0) {
+      if (chunk_start(my_n - 1) + CT > s1)
+        run_chunk(my_n - 1, std::true_type{}, std::false_type{});
+      else
+        run_chunk(my_n - 1, std::false_type{}, std::false_type{});
+    }
+
+    // Wave result: rows share m_ref, so value sums add without rescaling; l adds
+    // over the lanes holding the same head.
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float x = acc[g][k];
+        if constexpr (LPT == 8) x += ror<8>(x);
+        x = sum_swap16(x);
+        acc[g][k] = sum_swap32(x);
+      }
+    const float l_wave = class_sum<G>(l_part);      // lanes l = g (mod G) hold head g
+    wave_bad = __any(bad);
+    __syncthreads();                                 // transpose area becomes sm_acc
+    if (row == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sm_acc(wave, g, col * 8 + k) = acc[g][k];
+    }
+    if (lane < G) {
+      sm_m[wave][lane] = m_ref;
+      sm_l[wave][lane] = l_wave;
+    }
   }
   if (lane == 0) sm_flag[wave] = wave_bad ? 1 : 0;
   __syncthreads();
