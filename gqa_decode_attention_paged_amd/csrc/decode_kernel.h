@@ -79,9 +79,10 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t num_blocks;
   int32_t max_blocks;
-  int32_t max_splits;
+  int32_t max_splits;           // row stride of the split partials
   int32_t hint_ctx;             // host bound on context lengths (sizes the grid)
   int32_t target_splits;        // split-count target of the split plan
+  int32_t proportional;         // slots shared out by sequence length (2 <= B <= 64)
   float scale_log2;             // softmax_scale * log2(e)
 };
 
@@ -116,6 +117,14 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+// Wave-wide sum in double; exact (hence order-independent) for integer values
+// whose sum stays below 2^53.
+__device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
   return x;
@@ -271,23 +280,12 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   static_assert(kWaveBytes % 16 == 0, "LDS alignment");
   using Vec = typename KVTraits<FP8>::Vec;
 
-  // Workgroup -> (split, KV head, sequence).  When the number of (sequence,
-  // KV head) pairs is a multiple of 8, all splits of one pair are placed on
-  // one XCD (workgroups are dealt to the 8 XCDs round robin).
+  // Workgroup -> (KV head, slot).  blockIdx.y is the KV head and the S * B
+  // workgroups (x, z) of one KV head are its slots.  Uniform allocation gives
+  // slot (x, z) to split x of sequence z; proportional allocation shares the
+  // slots out by sequence length (below).
   const int S = gridDim.x;
-  const int P = gridDim.y * gridDim.z;
-  const int lin = blockIdx.x + S * (blockIdx.y + gridDim.y * blockIdx.z);
-  int split, pair;
-  if ((P & 7) == 0) {
-    const int xcd = lin & 7, slot = lin >> 3;
-    pair = (slot / S) * 8 + xcd;
-    split = slot % S;
-  } else {
-    pair = lin / S;
-    split = lin % S;
-  }
-  const int kvh = pair % p.num_kv_heads;
-  const int b = pair / p.num_kv_heads;
+  const int kvh = blockIdx.y;
   const int h0 = kvh * G;
 
   const int tid = threadIdx.x;
@@ -314,9 +312,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   char* const sm_wave = sm_raw + wave * kWaveBytes;   // this wave's staging area
 
   // Speculative block-id prefetch: most batches have every sequence at the
-  // launch hint's length, so the ids of this wave's chunks under the hint's
-  // split plan are loaded together with the context length.
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks;
+  // launch hint's length, where slot (x, z) is split x of sequence z under the
+  // hint's split plan; the ids of this wave's chunks there are loaded together
+  // with the context lengths.
+  const int32_t* bt = p.block_tables + (size_t)blockIdx.z * p.max_blocks;
   auto load_ids = [&](int s0_, int s1_, int my_n_, int jbase) {
     const int jj = jbase + lane / EPC;
     const int tok = s0_ + (wave + jj * WAVES) * CT + (lane % EPC) * BS;
@@ -327,16 +326,59 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     return wave < nch ? (nch - wave + WAVES - 1) / WAVES : 0;
   };
   const SplitPlan hplan = split_plan(p.hint_ctx, p.target_splits);
-  const int hs0 = split * hplan.split_tokens;
+  const int hs0 = (int)blockIdx.x * hplan.split_tokens;
   const int hs1 = min(p.hint_ctx, hs0 + hplan.split_tokens);
-  const int hmy_n = split < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
+  const int hmy_n = (int)blockIdx.x < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
   int ids = load_ids(hs0, hs1, hmy_n, 0);
 
-  const int ctx = p.context_lens[b];
+  // This workgroup's sequence b, its split, and the number of slots b owns.
+  int b = blockIdx.z, split = blockIdx.x, slots_b = S, ctx, pos;
+  if (p.proportional) {
+    // Lane i holds sequence i.  When the lengths differ, sequence i gets
+    // n_i = 1 + floor(R c_i / sum c) slots (invalid lengths weigh 0), R the
+    // largest value in [S*B - B, S*B] for which the n_i fit the S*B slots.
+    // Every wave computes the same result; the sum is exact, so n_i does not
+    // depend on the batch order.  Equal lengths keep the uniform plan (which
+    // the sharing would also give: n_i = S).
+    const int nseq = gridDim.z;
+    const int ci = lane < nseq ? p.context_lens[lane] : 0;
+    const int pi = (p.positions && lane < nseq) ? p.positions[lane] : -1;
+    const int c0 = __builtin_amdgcn_readfirstlane(ci);
+    if (__ballot(lane < nseq && ci != c0) != 0) {    // lengths differ: share out
+      const int cw = (ci > 0 && ci <= p.hint_ctx && ci <= p.max_blocks * BS) ? ci : 0;
+      const double tot = wave_sum_f64((double)cw);
+      const double f = tot > 0.0 ? (double)cw / tot : 0.0;
+      const int slots = S * nseq;
+      int lo = slots - nseq, hi = slots;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const float cnt = lane < nseq ? (float)(1 + (int)floor((double)mid * f)) : 0.f;
+        if (class_sum<1>(cnt) <= (float)slots) lo = mid; else hi = mid - 1;
+      }
+      const int ni = lane < nseq ? min(1 + (int)floor((double)lo * f), p.max_splits) : 0;
+      int incl = ni;                                 // inclusive prefix sum over lanes
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += t;
+      }
+      const int slot = (int)blockIdx.x + S * (int)blockIdx.z;
+      b = __builtin_amdgcn_readfirstlane(
+          __builtin_popcountll(__ballot(lane < nseq && incl <= slot)));
+      if (b >= nseq) return;                         // a slot the rounding left over
+      split = slot - (b > 0 ? __builtin_amdgcn_readlane(incl, b - 1) : 0);
+      slots_b = __builtin_amdgcn_readlane(ni, b);
+      bt = p.block_tables + (size_t)b * p.max_blocks;
+    }
+    ctx = __builtin_amdgcn_readlane(ci, b);
+    pos = __builtin_amdgcn_readlane(pi, b);
+  } else {
+    ctx = p.context_lens[b];
+    pos = p.positions ? p.positions[b] : -1;
+  }
   const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS;
-  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx, p.target_splits);
-  const bool too_long = plan.num_splits > p.max_splits;
-  const int pos = p.positions ? p.positions[b] : -1;
+  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx, p.proportional ? slots_b : p.target_splits);
+  const bool too_long = ctx > p.hint_ctx || plan.num_splits > slots_b;
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
   const int owner = (!degenerate && pos >= 0 && pos < ctx) ? pos / plan.split_tokens : 0;
   const bool pos_in_split = !degenerate && pos >= 0 && pos < ctx;
@@ -377,7 +419,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
       wait_vector_memory();
     }
   }
-  if (s0 != hs0 || s1 != hs1) ids = load_ids(s0, s1, my_n, 0);   // hint did not apply
+  if (b != (int)blockIdx.z || s0 != hs0 || s1 != hs1)
+    ids = load_ids(s0, s1, my_n, 0);               // the speculation did not apply
 
   // Online-softmax state shared by both paths: m_ref, the reference max of this
   // lane's head (wave-uniform per head), and l_part, this lane's share of that

@@ -262,10 +262,15 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
   const int target = target_splits(s, fn, waves * 64);
-  int max_splits = gqa::split_plan(max_context_len, target).num_splits;
-  if (max_splits < 1) max_splits = 1;
-  if ((int64_t)max_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
+  int launch_splits = gqa::split_plan(max_context_len, target).num_splits;
+  if (launch_splits < 1) launch_splits = 1;
+  if ((int64_t)launch_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  // Ragged batches: share each KV head's slots out by sequence length (one
+  // lane per sequence, so up to 64 sequences) instead of giving every sequence
+  // the same number of splits.
+  const bool proportional = !(s->flags & GQA_FLAG_BATCH_INVARIANT) && launch_splits >= 2 &&
+                            s->num_seqs >= 2 && s->num_seqs <= 64;
 
   char* ws = static_cast<char*>(workspace);
   gqa::DecodeParams p;
@@ -288,11 +293,12 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   p.num_kv_heads = s->num_kv_heads;
   p.num_blocks = s->num_blocks;
   p.max_blocks = s->max_blocks_per_seq;
-  p.max_splits = max_splits;
+  p.max_splits = max_splits_for(max_context_len);
   p.hint_ctx = max_context_len;
   p.target_splits = target;
+  p.proportional = proportional ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  st = launch(fn, dim3(max_splits, s->num_kv_heads, s->num_seqs), dim3(waves * 64), &p,
+  st = launch(fn, dim3(launch_splits, s->num_kv_heads, s->num_seqs), dim3(waves * 64), &p,
               "paged_decode", stream);
   return st == GQA_OK ? ok() : st;
 }

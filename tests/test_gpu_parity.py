@@ -87,6 +87,67 @@ def test_empty_and_mixed_batch(gpu):
     assert_parity(out, lse, ref, ref_lse, "mixed")
 
 
+@pytest.mark.parametrize("lens", [
+    [9000] + [3] * 19,                                       # one long among many tiny
+    [1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987, 1597, 2584, 4181],
+])
+def test_ragged_batch_shares_workgroups(gpu, lens):
+    """Ragged batches share each KV head's workgroups out by length; every sequence
+    still matches the oracle."""
+    spec = small_spec(num_seqs=len(lens), num_q_heads=16, num_kv_heads=4, head_dim=128,
+                      block_size=16, context=max(lens), case_id=2800 + len(lens))
+    case = make_case(spec, seed=10, context_lens=lens)
+    ref, ref_lse = run_oracle(case)
+    out, lse = run_step(gpu, to_device(case), case)
+    assert_parity(out, lse, ref, ref_lse, f"ragged {len(lens)}")
+
+
+@pytest.mark.parametrize("nseq", [64, 65])
+def test_ragged_batch_at_the_lane_limit(gpu, nseq):
+    """64 sequences (the most one wave shares out) and 65 (the uniform plan)."""
+    lens = np.random.default_rng(nseq).integers(1, 1500, nseq).tolist()
+    spec = small_spec(num_seqs=nseq, num_q_heads=8, num_kv_heads=1, head_dim=64,
+                      block_size=16, context=1500, case_id=2900 + nseq)
+    case = make_case(spec, seed=11, context_lens=lens)
+    ref, ref_lse = run_oracle(case)
+    out, lse = run_step(gpu, to_device(case), case)
+    assert_parity(out, lse, ref, ref_lse, f"{nseq} sequences")
+
+
+def test_ragged_batch_with_invalid_lengths(gpu):
+    """Invalid lengths inside a ragged batch: those sequences get NaN (negative, or
+    longer than the launch hint), an empty one gets zeros, the rest match the oracle."""
+    spec = small_spec(num_seqs=6, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                      block_size=16, context=2000, case_id=3000)
+    case = make_case(spec, seed=12, context_lens=[500, 10, 1200, 1500, 0, 70])
+    ref, ref_lse = run_oracle(case)
+    bad = dict(case)
+    bad["context_lens"] = case["context_lens"].copy()
+    bad["context_lens"][1] = -3
+    out, lse = run_step(gpu, to_device(bad), bad, max_context_len=1400)   # 1500 > hint
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
+    assert np.all(np.isnan(out[3])) and np.all(np.isnan(lse[3]))
+    assert np.all(out[4] == 0) and np.all(lse[4] == -np.inf)
+    keep = [0, 2, 5]
+    assert_parity(out[keep], lse[keep], ref[keep], ref_lse[keep], "valid sequences")
+
+
+def test_fused_append_ragged_batch(gpu):
+    """The fused append with a ragged batch: each sequence's new token is committed by
+    the workgroup that owns its slot, and attention matches the oracle."""
+    lens = [3000, 17, 700, 1, 2048, 129]
+    spec = small_spec(num_seqs=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      block_size=16, context=max(lens), append=True, case_id=3100)
+    case = make_case(spec, seed=13, context_lens=lens)
+    ref, ref_lse = run_oracle(case)
+    dev = to_device(case)
+    out, lse = run_fused_step(gpu, dev, case)
+    assert_parity(out, lse, ref, ref_lse, "fused ragged")
+    k = dev["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    v = dev["v_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(k, case["k_pool_full"]) and np.array_equal(v, case["v_pool_full"])
+
+
 def test_zero_sequences_is_a_no_op(gpu):
     import torch
     spec = small_spec(num_seqs=1, context=20, case_id=2300)
