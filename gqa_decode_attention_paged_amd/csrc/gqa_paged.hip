@@ -150,9 +150,10 @@ int resident_workgroups(const void* fn, int threads) {
   return cap;
 }
 
-// Split-count target.  By default, enough splits that the batch's (sequence,
-// KV head) pairs fill the resident-workgroup capacity once (fewer, longer
-// splits amortise each workgroup's start-up and merge).  With
+// Split-count target.  By default, as many splits as let the batch's (sequence,
+// KV head) pairs fill the resident-workgroup capacity once without exceeding
+// it (fewer, longer splits amortise each workgroup's start-up and merge, and a
+// partial second round of workgroups would only add a tail).  With
 // GQA_FLAG_BATCH_INVARIANT, the fixed maximum, so the split of a sequence
 // depends on its own length only.
 int target_splits(const gqa_paged_shape* s, const void* fn, int threads) {
@@ -160,7 +161,7 @@ int target_splits(const gqa_paged_shape* s, const void* fn, int threads) {
   const int cap = resident_workgroups(fn, threads);
   if (cap <= 0) return gqa::kMaxSplits;
   const int64_t pairs = (int64_t)s->num_seqs * s->num_kv_heads;
-  int64_t t = (cap + pairs - 1) / pairs;
+  int64_t t = cap / pairs;            // never more workgroups than fit at once
   if (t < 1) t = 1;
   if (t > gqa::kMaxSplits) t = gqa::kMaxSplits;
   return (int)t;
