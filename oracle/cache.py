@@ -55,3 +55,24 @@ def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: 
         k_out[blk, :, slot, :] = k_new[b]
         v_out[blk, :, slot, :] = v_new[b]
     return k_out, v_out
+
+
+def kv_append_tokens(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
+                     v_new: np.ndarray, block_tables: np.ndarray, positions: np.ndarray,
+                     block_size: int):
+    """Write T tokens per sequence: ``k_new/v_new`` ``[B][T][H_kv][d_h]`` at logical
+    positions ``[B][T]``.  A position outside the table's range, or whose table
+    entry is not a block of the pool, writes nothing.  Returns new pools."""
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    capacity = block_tables.shape[1] * block_size
+    for b in range(positions.shape[0]):
+        for j in range(positions.shape[1]):
+            pos = int(positions[b, j])
+            if pos < 0 or pos >= capacity:
+                continue
+            blk = int(block_tables[b][pos // block_size])
+            if blk < 0 or blk >= k_pool.shape[0]:
+                continue
+            k_out[blk, :, pos % block_size, :] = k_new[b, j]
+            v_out[blk, :, pos % block_size, :] = v_new[b, j]
+    return k_out, v_out

@@ -243,6 +243,57 @@ def make_case(spec: Spec | str, seed: int = 0, *, context_lens=None,
     return out
 
 
+def make_multi_query_case(spec: Spec | str, num_queries: int, seed: int = 0, *,
+                          context_lens=None, append: bool = True, poison: bool = True) -> dict:
+    """A case with ``num_queries`` consecutive query positions per sequence.
+
+    The base pools, tables and lengths are ``make_case`` of ``spec`` without its
+    single-token append.  ``q`` is ``[B][Q][H_q][d]`` bf16 from its own seeded
+    stream; query i of sequence b sits at position ``ctx_b - Q + i``.  With
+    ``append`` the last Q tokens of every sequence are the step's new tokens:
+    ``k_new``/``v_new`` are ``[B][Q][H_kv][d]``, ``positions`` ``[B][Q]`` (-1 where
+    ``ctx_b - Q + i < 0``), and ``k_pool``/``v_pool`` hold NaN codes in those
+    slots until the append fills them (``k_pool_full``/``v_pool_full`` hold them).
+    """
+    if isinstance(spec, str):
+        spec = SPECS[spec]
+    base = Spec(spec.name, spec.case_id, spec.num_seqs, spec.num_q_heads, spec.num_kv_heads,
+                spec.head_dim, spec.block_size, kv_dtype=spec.kv_dtype, context=spec.context,
+                append=False, pool=spec.pool)
+    case = make_case(base, seed, context_lens=context_lens, poison=poison)
+    Q = int(num_queries)
+    B = case["context_lens"].shape[0]
+    Hq, Hkv, D, BS = spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, spec.case_id, 1])))
+    case["q"] = _normal_bf16(rng, (B, Q, Hq, D))
+    case["num_queries"] = Q
+    ctx = case["context_lens"].astype(np.int64)
+    positions = (ctx[:, None] - Q + np.arange(Q)[None, :]).astype(np.int32)
+    positions[positions < 0] = -1
+    case["positions"] = positions
+    if append:
+        if spec.kv_dtype != "bf16":
+            raise ValueError("append workloads are bf16")
+        kf, vf = case["k_pool_full"], case["v_pool_full"]
+        k_new = np.zeros((B, Q, Hkv, D), dtype=np.uint16)
+        v_new = np.zeros((B, Q, Hkv, D), dtype=np.uint16)
+        k_pool, v_pool = kf.copy(), vf.copy()
+        for b in range(B):
+            for i in range(Q):
+                p = int(positions[b, i])
+                if p < 0:
+                    continue
+                blk, slot = case["block_tables"][b, p // BS], p % BS
+                k_new[b, i] = kf[blk, :, slot, :]
+                v_new[b, i] = vf[blk, :, slot, :]
+                if poison:
+                    k_pool[blk, :, slot, :] = BF16_NAN
+                    v_pool[blk, :, slot, :] = BF16_NAN
+        case["k_new"], case["v_new"] = k_new, v_new
+        case["k_pool"], case["v_pool"] = k_pool, v_pool
+    return case
+
+
 def _fp8_pool(rng, shape, valid):
     """N(0,1) float32 source values -> fp8 codes + per-(block, head) scale amax/448."""
     NB, H, BS, D = shape
