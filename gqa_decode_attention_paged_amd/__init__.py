@@ -65,6 +65,14 @@ def load():
     S = ctypes.POINTER(PagedShape)
     lib.gqa_kv_append.argtypes = [S, _P, _P, _P, _P, _P, _P, _P]
     lib.gqa_kv_append.restype = ctypes.c_int
+    lib.gqa_kv_append_tokens.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]
+    lib.gqa_kv_append_tokens.restype = ctypes.c_int
+    lib.gqa_paged_multi_query_workspace_size.argtypes = [S, ctypes.c_int32, ctypes.c_int32]
+    lib.gqa_paged_multi_query_workspace_size.restype = ctypes.c_size_t
+    lib.gqa_paged_decode_multi_query.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                                 ctypes.c_int32, ctypes.c_float, _P, _P, _P,
+                                                 ctypes.c_size_t, _P]
+    lib.gqa_paged_decode_multi_query.restype = ctypes.c_int
     lib.gqa_decode_num_splits.argtypes = [ctypes.c_int32]
     lib.gqa_decode_num_splits.restype = ctypes.c_int32
     lib.gqa_paged_decode_workspace_size.argtypes = [S, ctypes.c_int32]
@@ -141,6 +149,48 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions):
     _check(lib.gqa_kv_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                              _ptr(v_cache), _ptr(block_tables), _ptr(positions),
                              _stream(k_cache)))
+
+
+def kv_append_tokens(k_new, v_new, k_cache, v_cache, block_tables, positions):
+    """Write T new tokens per sequence ([B][T][H_kv][d_h] rows at positions [B][T])."""
+    lib = load()
+    B, T = k_new.shape[0], k_new.shape[1]
+    shape = make_shape(B, k_cache.shape[1], k_cache, block_tables)
+    _check(lib.gqa_kv_append_tokens(ctypes.byref(shape), int(T), _ptr(k_new), _ptr(v_new),
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                    _ptr(positions), _stream(k_cache)))
+
+
+def multi_query_workspace_size(shape: PagedShape, num_queries: int, max_context_len: int) -> int:
+    return int(load().gqa_paged_multi_query_workspace_size(ctypes.byref(shape), int(num_queries),
+                                                           int(max_context_len)))
+
+
+def paged_decode_multi_query(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                             softmax_scale=None, k_scale=None, v_scale=None, out=None,
+                             out_lse=None, workspace=None, return_lse=True,
+                             batch_invariant=False):
+    """Attention for Q consecutive query positions per sequence, q [B][Q][H_q][d_h]: query i
+    sits at position context_lens[b] - Q + i and attends causally.  Returns (out, lse)."""
+    import torch
+    lib = load()
+    B, Q, Hq, D = q.shape
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Q, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = multi_query_workspace_size(shape, Q, max_context_len)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.gqa_paged_decode_multi_query(
+        ctypes.byref(shape), int(Q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, out_lse
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_context_len,

@@ -60,7 +60,7 @@
 namespace gqa {
 
 struct DecodeParams {
-  const uint16_t* q;            // [B][Hq][D] bf16
+  const uint16_t* q;            // [B][Q][Hq][D] bf16
   void* k_cache;                // [NB][Hkv][BS][D]; written only by the fused append
   void* v_cache;
   const float* k_scale;         // [NB][Hkv] (fp8 only)
@@ -70,13 +70,17 @@ struct DecodeParams {
   const uint16_t* k_new;        // [B][Hkv][D] fused append, or null
   const uint16_t* v_new;
   const int32_t* positions;     // [B] slot of the appended token, or null
-  float* out;                   // [B][Hq][D]
-  float* out_lse;               // [B][Hq] or null
-  float* ws_o;                  // [B][Hkv][max_splits][G][D] partial outputs (normalised)
-  float* ws_lse;                // [B][Hkv][max_splits][G]    partial base-2 lse
+  float* out;                   // [B][Q][Hq][D]
+  float* out_lse;               // [B][Q][Hq] or null
+  float* ws_o;                  // [B][Hkv][max_splits][M][D] partial outputs (normalised)
+  float* ws_lse;                // [B][Hkv][max_splits][M]    partial base-2 lse
   uint32_t* counters;           // [B][Hkv] arrivals, kCounterStride words apart; zero between calls
   int32_t num_q_heads;
   int32_t num_kv_heads;
+  int32_t group;                // G = num_q_heads / num_kv_heads (a power of two)
+  int32_t group_shift;          // log2(G)
+  int32_t num_queries;          // Q query positions per sequence (the last Q tokens)
+  int32_t rows;                 // R = G * Q rows per (sequence, KV head)
   int32_t num_blocks;
   int32_t max_blocks;
   int32_t max_splits;           // row stride of the split partials
@@ -244,28 +248,32 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
 }
 
-template <int D, int BS, int G, bool FP8, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParams p) {
-  // bf16 groups of two or more query heads use the matrix path; fp8 pools and
-  // single-head groups the vector path.
-  constexpr bool MFMA = !FP8 && G >= 2;
+template <int D, int BS, int M, bool FP8, int WAVES>
+// Launch bounds ask for two resident waves per SIMD (one 8-wave or two 4-wave
+// workgroups per CU), which caps registers at 256 per lane.
+__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(DecodeParams p) {
+  // M is the row capacity: the rows of one (sequence, KV head) are its query
+  // positions times its G query heads, row m = i*G + g (R = G*Q <= M of them).
+  // bf16 pools with two or more rows use the matrix path; fp8 pools and single
+  // rows the vector path.
+  constexpr bool MFMA = !FP8 && M >= 2;
   constexpr int LPT = D / 8;                 // lanes per token row (8 elements each)
   constexpr int TPI = kWave / LPT;           // rows per row-layout load instruction
-  constexpr int CT = (MFMA || G < 8) ? 32 : 16;   // tokens per wave chunk
+  constexpr int CT = (MFMA || M < 8) ? 32 : 16;   // tokens per wave chunk
   constexpr int NI = CT / TPI;               // row-layout loads per chunk
   constexpr int EPC = CT >= BS ? CT / BS : 1;  // block-table entries per chunk
   constexpr int CPG = kWave / EPC;           // chunks per preloaded table group
   constexpr int ESZ = KVTraits<FP8>::kBytes;
   constexpr int NT = WAVES * kWave;
-  // Vector path.  LDS score transpose: partial dot products of token t, head g,
-  // lane column c at t*PSTR + g*GSTR + c; the weights p[t][g] at t*G + g.
-  constexpr int NPAIR = CT * G;              // (token, head) scores per chunk
+  // Vector path.  LDS score transpose: partial dot products of token t, row g,
+  // lane column c at t*PSTR + g*GSTR + c; the weights p[t][g] at t*M + g.
+  constexpr int NPAIR = CT * M;              // (token, row) scores per chunk
   constexpr int PPL = (NPAIR + kWave - 1) / kWave;   // scores per lane
-  constexpr int TSTEP = kWave / G;           // token stride between a lane's scores
+  constexpr int TSTEP = kWave / M;           // token stride between a lane's scores
   constexpr int GSTR = LPT + 4;
-  constexpr int PSTR = G * GSTR + 4;
+  constexpr int PSTR = M * GSTR + 4;
   constexpr int kPartFloats = CT * PSTR;
-  constexpr int kValuWaveBytes = (kPartFloats + NPAIR + 4 * ((G + 3) / 4)) * 4;
+  constexpr int kValuWaveBytes = (kPartFloats + NPAIR + 4 * ((M + 3) / 4)) * 4;
   // Matrix path: 16x16x32 bf16 MFMA tiles.  Staged V rows are VSTR elements
   // apart (a shift of 8 banks per row for the transpose reads).
   constexpr int KB = D / 32;                 // k-steps of the score product
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   constexpr int kMfmaWaveBytes = CT * VSTR * 2 + 16 * PRS * 4 + 16 * 4;
   constexpr int kWaveBytes = MFMA ? kMfmaWaveBytes : kValuWaveBytes;
   static_assert(BS % TPI == 0 && BS % 16 == 0 && kChunkTokens % CT == 0, "tile geometry");
-  static_assert(kWave % G == 0 && PPL * TSTEP * G >= NPAIR && G <= 16, "score mapping");
+  static_assert(kWave % M == 0 && PPL * TSTEP * M >= NPAIR && M <= 16, "score mapping");
   static_assert(kWaveBytes % 16 == 0, "LDS alignment");
   using Vec = typename KVTraits<FP8>::Vec;
 
@@ -286,6 +294,9 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   // slots out by sequence length (below).
   const int S = gridDim.x;
   const int kvh = blockIdx.y;
+  const int G = p.group;                     // query heads per KV head
+  const int Q = p.num_queries;               // query positions per sequence
+  const int R = p.rows;                      // rows in use, G*Q
   const int h0 = kvh * G;
 
   const int tid = threadIdx.x;
@@ -296,19 +307,19 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
 
   // LDS: per-wave chunk staging during the loop; afterwards (reused) the
   // per-wave partial sums, then the split weights and float4 sums of the merge.
-  constexpr int C4 = G * D / 4;                    // float4 columns of one head group
+  constexpr int C4 = M * D / 4;                    // float4 columns of M rows
   constexpr int SP = NT >= C4 ? NT / C4 : 1;       // threads per column in the final merge
-  constexpr int kAccBytes = WAVES * G * D * 4;
-  constexpr int kMergeBytes = (G * kWave + 4 * ((G + 3) / 4) + 4 * SP * C4) * 4;
+  constexpr int kAccBytes = WAVES * M * D * 4;
+  constexpr int kMergeBytes = (M * kWave + 4 * ((M + 3) / 4) + 4 * SP * C4) * 4;
   constexpr int kLoopBytes = WAVES * kWaveBytes;
   constexpr int kBufA = kAccBytes > kMergeBytes ? kAccBytes : kMergeBytes;
   constexpr int kBufBytes = kBufA > kLoopBytes ? kBufA : kLoopBytes;
   __shared__ __attribute__((aligned(16))) char sm_raw[kBufBytes];
-  __shared__ float sm_m[WAVES][G];
-  __shared__ float sm_l[WAVES][G];
+  __shared__ float sm_m[WAVES][M];
+  __shared__ float sm_l[WAVES][M];
   __shared__ int sm_flag[WAVES + 1];
   float* const sm_buf = reinterpret_cast<float*>(sm_raw);
-  auto sm_acc = [&](int w, int g, int d) -> float& { return sm_buf[(w * G + g) * D + d]; };
+  auto sm_acc = [&](int w, int g, int d) -> float& { return sm_buf[(w * M + g) * D + d]; };
   char* const sm_wave = sm_raw + wave * kWaveBytes;   // this wave's staging area
 
   // Speculative block-id prefetch: most batches have every sequence at the
@@ -376,8 +387,17 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     ctx = p.context_lens[b];
     pos = p.positions ? p.positions[b] : -1;
   }
-  const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS;
+  // A sequence holds its Q query positions as its last Q tokens, so 0 < ctx < Q
+  // is invalid (ctx = 0 stays the empty sequence).
+  const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS || (ctx > 0 && ctx < Q);
   const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx, p.proportional ? slots_b : p.target_splits);
+  // Row m of this (sequence, KV head) is query i = m / G of head h0 + m % G; its
+  // flat index into q [B][Q][H_q][D], out and out_lse.  Query i sits at position
+  // ctx - Q + i and attends to the tokens before it and itself.
+  auto row_index = [&](int m) -> size_t {
+    return ((size_t)b * Q + (m >> p.group_shift)) * p.num_q_heads + h0 + (m & (G - 1));
+  };
+  auto row_limit = [&](int m) { return ctx - Q + 1 + (m >> p.group_shift); };   // tokens < this
   const bool too_long = ctx > p.hint_ctx || plan.num_splits > slots_b;
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
   const int owner = (!degenerate && pos >= 0 && pos < ctx) ? pos / plan.split_tokens : 0;
@@ -388,10 +408,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     if (split != 0) return;
     const bool bad = ctx_bad || too_long;
     const float v = bad ? __builtin_nanf("") : 0.f;
-    for (int i = tid; i < G * D; i += NT)
-      p.out[((size_t)b * p.num_q_heads + h0) * D + i] = v;
-    if (p.out_lse && tid < G)
-      p.out_lse[(size_t)b * p.num_q_heads + h0 + tid] = bad ? __builtin_nanf("") : kNegInf;
+    for (int i = tid; i < R * D; i += NT) p.out[row_index(i / D) * D + i % D] = v;
+    if (p.out_lse && tid < R) p.out_lse[row_index(tid)] = bad ? __builtin_nanf("") : kNegInf;
     return;
   }
   const int nsplit = plan.num_splits;
@@ -491,15 +509,15 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     float* sm_pw = reinterpret_cast<float*>(sm_wave + CT * VSTR * 2);  // [16][PRS] weights
     float* sm_alpha = sm_pw + 16 * PRS;                                // [16] rescale factors
 
-    bf16x8_t qop[KB];                     // q of head hd, dims 8*qd + 32*kb .. +7
+    bf16x8_t qop[KB];                     // q of row hd, dims 8*qd + 32*kb .. +7
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (hd < G)
-        v = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.num_q_heads + h0 + hd) * D +
-                                            8 * qd + 32 * kb);
+      if (hd < R)
+        v = *reinterpret_cast<const uint4*>(p.q + row_index(hd) * D + 8 * qd + 32 * kb);
       qop[kb] = as_bf16x8(v);
     }
+    const int hd_limit = hd < R ? row_limit(hd) : 0;   // this lane's row sees tokens < this
     f32x4 acc[NN];                        // rows: heads 4*qd + r; columns: dims 16*n + hd
 #pragma unroll
     for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -531,6 +549,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
       constexpr bool NEXT = decltype(next_tag)::value;   // chunk j+1 exists
       const int t0 = chunk_start(j);
       const int nvalid = s1 - t0;
+      const int lim = min(nvalid, hd_limit - t0);        // tokens t < lim count for row hd
       f32x4 sc[2];
 #pragma unroll
       for (int t16 = 0; t16 < 2; ++t16) {
@@ -554,7 +573,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * t16 + 4 * qd + r;
           float x = sc[t16][r] * p.scale_log2;
-          if (hd >= G || (SLOW && t >= nvalid)) x = kNegInf;
+          if (t >= lim) x = kNegInf;           // split tail, causal limit, unused rows
           s[t16 * 4 + r] = x;
           cmax = fmaxf(cmax, x);
         }
@@ -647,8 +666,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     for (int n = 0; n < NN; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (4 * qd + r < G) sm_acc(wave, 4 * qd + r, 16 * n + hd) = acc[n][r];
-    if (lane < G) {
+        if (4 * qd + r < R) sm_acc(wave, 4 * qd + r, 16 * n + hd) = acc[n][r];
+    if (lane < R) {
       sm_m[wave][lane] = m_ref;
       sm_l[wave][lane] = l_wave;
     }
@@ -656,16 +675,16 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     // ---- Vector path.  LPT lanes hold one token row (8 elements each); partial
     // dot products go through LDS so each lane finishes whole scores.
     float* sm_part = reinterpret_cast<float*>(sm_wave);   // transpose area
-    float* sm_pw = sm_part + kPartFloats;                 // [CT][G] weights
-    float* sm_alpha = sm_pw + NPAIR;                      // [G] rescale factors
+    float* sm_pw = sm_part + kPartFloats;                 // [CT][M] weights
+    float* sm_alpha = sm_pw + NPAIR;                      // [M] rescale factors
 
-    // q: this lane's 8 dims of each of the G heads.
-    const uint16_t* qp = p.q + ((size_t)b * p.num_q_heads + h0) * D + col * 8;
-    uint32_t qw[G][4];
-    float qf[FP8 ? G : 1][8];
+    // q: this lane's 8 dims of each of the M rows (rows >= R are zero).
+    uint32_t qw[M][4];
+    float qf[FP8 ? M : 1][8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + (size_t)g * D);
+    for (int g = 0; g < M; ++g) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (g < R) v = *reinterpret_cast<const uint4*>(p.q + row_index(g) * D + col * 8);
       qw[g][0] = v.x; qw[g][1] = v.y; qw[g][2] = v.z; qw[g][3] = v.w;
       if constexpr (FP8) {
 #pragma unroll
@@ -675,25 +694,27 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         }
       }
     }
-    // This lane's scores are for head sg = lane % G; acc holds the value sums
+    // This lane's scores are for row sg = lane % M; acc holds the value sums
     // of this lane's 8 dims.
-    const int sg = lane % G;
-    float acc[G][8];
+    const int sg = lane % M;
+    const int sg_limit = sg < R ? row_limit(sg) : 0;     // row sg sees tokens < this
+    float acc[M][8];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < M; ++g)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
     Vec kr[NI], vr[NI];
     float ks[NI], vs[NI];
 
     // One chunk: partial dot products -> LDS; each lane sums and exponentiates its
-    // own (token, head) scores; weights -> LDS; value sums.  SLOW handles the
-    // split's tail chunk (rows past the end); the fast path has no per-row selects.
+    // own (token, row) scores; weights -> LDS; value sums.  SLOW handles the
+    // split's tail chunk (V rows past the end are zeroed).
     auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
       constexpr bool SLOW = decltype(slow_tag)::value;
       constexpr bool NEXT = decltype(next_tag)::value;     // chunk j+1 exists
       const int t0 = chunk_start(j);
       const int nvalid = s1 - t0;                      // rows t < nvalid are real
+      const int lim = min(nvalid, sg_limit - t0);      // tokens t < lim count for row sg
       if constexpr (SLOW) {
         // zero V rows past the split end (their slots may hold NaN poison)
 #pragma unroll
@@ -704,12 +725,12 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const Vec kk = kr[i];
-        float part[G];
+        float part[M];
         if constexpr (FP8) {
           float kf[8];
           widen8<true>(kk, kf);
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
+          for (int g = 0; g < M; ++g) {
             float a = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) a = fmaf(qf[g][k], kf[k], a);
@@ -717,7 +738,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
           }
         } else {
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
+          for (int g = 0; g < M; ++g) {
             float a = dot2_bf16(qw[g][0], kk.x, 0.f);
             a = dot2_bf16(qw[g][1], kk.y, a);
             a = dot2_bf16(qw[g][2], kk.z, a);
@@ -726,7 +747,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         }
         float* dst = sm_part + (i * TPI + row) * PSTR + col;
 #pragma unroll
-        for (int g = 0; g < G; ++g) dst[g * GSTR] = part[g];
+        for (int g = 0; g < M; ++g) dst[g * GSTR] = part[g];
       }
       __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
       if constexpr (NEXT) {
@@ -734,12 +755,12 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         issue_rows(j + 1, kbase, kr, ks, p.k_scale, true);
       }
       __builtin_amdgcn_wave_barrier();
-      // this lane's scores: token t = lane / G + q * TSTEP, head sg
+      // this lane's scores: token t = lane / M + q * TSTEP, row sg
       float sc[PPL];
       float cmax = kNegInf;
 #pragma unroll
       for (int q = 0; q < PPL; ++q) {
-        const int t = lane / G + q * TSTEP;
+        const int t = lane / M + q * TSTEP;
         float tot = kNegInf;
         if (t < CT) {
           const float4* src = reinterpret_cast<const float4*>(sm_part + t * PSTR + sg * GSTR);
@@ -750,36 +771,36 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
             a += (v.x + v.y) + (v.z + v.w);
           }
           tot = a * p.scale_log2;
-          if (SLOW && t >= nvalid) tot = kNegInf;
+          if (t >= lim) tot = kNegInf;         // split tail, causal limit, unused rows
         }
         sc[q] = tot;
         cmax = fmaxf(cmax, tot);
       }
-      cmax = class_max<G>(cmax);                     // chunk max of head sg, wave-wide
+      cmax = class_max<M>(cmax);                     // chunk max of row sg, wave-wide
       // lazy rescale: only when the chunk max passes the reference by 2^kLazyLog2
       const bool need = cmax > m_ref + kLazyLog2;
       const bool any_need = __any(need);
       if (any_need) {
         const float m_new = need ? cmax : m_ref;
-        const float alpha = fast_exp2(m_ref - m_new);   // 0 while m_ref = -inf; 1 if kept
+        const float alpha = m_new == m_ref ? 1.f : fast_exp2(m_ref - m_new);  // 0 from -inf
         l_part *= alpha;
         m_ref = m_new;
-        if (lane < G) sm_alpha[lane] = alpha;
+        if (lane < M) sm_alpha[lane] = alpha;
       }
 #pragma unroll
       for (int q = 0; q < PPL; ++q) {
-        const int t = lane / G + q * TSTEP;
-        const float pw = (!SLOW || sc[q] > kNegInf) ? fast_exp2(sc[q] - m_ref) : 0.f;
+        const int t = lane / M + q * TSTEP;
+        const float pw = sc[q] > kNegInf ? fast_exp2(sc[q] - m_ref) : 0.f;
         l_part += (t < CT) ? pw : 0.f;
-        if (t < CT) sm_pw[t * G + sg] = pw;
+        if (t < CT) sm_pw[t * M + sg] = pw;
       }
       __builtin_amdgcn_wave_barrier();
       if (any_need) {
-        float al[G];
+        float al[M];
 #pragma unroll
-        for (int g = 0; g < G; ++g) al[g] = sm_alpha[g];
+        for (int g = 0; g < M; ++g) al[g] = sm_alpha[g];
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < M; ++g)
 #pragma unroll
           for (int k = 0; k < 8; ++k) acc[g][k] *= al[g];
       }
@@ -788,20 +809,20 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
       for (int i = 0; i < NI; ++i) {
         float vf[8];
         widen8<FP8>(vr[i], vf);
-        float pw[G];
-        const float* src = sm_pw + (i * TPI + row) * G;
-        if constexpr (G % 4 == 0) {
+        float pw[M];
+        const float* src = sm_pw + (i * TPI + row) * M;
+        if constexpr (M % 4 == 0) {
 #pragma unroll
-          for (int g4 = 0; g4 < G / 4; ++g4) {
+          for (int g4 = 0; g4 < M / 4; ++g4) {
             const float4 v = reinterpret_cast<const float4*>(src)[g4];
             pw[4 * g4] = v.x; pw[4 * g4 + 1] = v.y; pw[4 * g4 + 2] = v.z; pw[4 * g4 + 3] = v.w;
           }
         } else {
 #pragma unroll
-          for (int g = 0; g < G; ++g) pw[g] = src[g];
+          for (int g = 0; g < M; ++g) pw[g] = src[g];
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < M; ++g) {
           const float pg = FP8 ? pw[g] * vs[i] : pw[g];
 #pragma unroll
           for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pg, vf[k], acc[g][k]);
@@ -832,7 +853,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
     // Wave result: rows share m_ref, so value sums add without rescaling; l adds
     // over the lanes holding the same head.
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < M; ++g)
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         float x = acc[g][k];
@@ -840,16 +861,16 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         x = sum_swap16(x);
         acc[g][k] = sum_swap32(x);
       }
-    const float l_wave = class_sum<G>(l_part);      // lanes l = g (mod G) hold head g
+    const float l_wave = class_sum<M>(l_part);      // lanes l = g (mod M) hold row g
     wave_bad = __any(bad);
     __syncthreads();                                 // transpose area becomes sm_acc
     if (row == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < M; ++g)
 #pragma unroll
         for (int k = 0; k < 8; ++k) sm_acc(wave, g, col * 8 + k) = acc[g][k];
     }
-    if (lane < G) {
+    if (lane < R) {
       sm_m[wave][lane] = m_ref;
       sm_l[wave][lane] = l_wave;
     }
@@ -862,28 +883,28 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) any_bad |= sm_flag[w];
   const size_t prow = ((size_t)b * p.num_kv_heads + kvh) * p.max_splits;   // partial rows
-  for (int idx = tid; idx < G * D; idx += NT) {
-    const int g = idx / D;
+  for (int idx = tid; idx < R * D; idx += NT) {
+    const int g = idx / D;                         // row
     const int d = idx % D;
-    float M = kNegInf;
+    float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm_m[w][g]);
+    for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, sm_m[w][g]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
       const float mw = sm_m[w][g];
-      const float a = mw > kNegInf ? fast_exp2(mw - M) : 0.f;
+      const float a = mw > kNegInf ? fast_exp2(mw - mx) : 0.f;
       L = fmaf(a, sm_l[w][g], L);
       O = fmaf(a, sm_acc(w, g, d), O);
     }
     const float o = O / L;
-    const float lse2 = any_bad ? __builtin_nanf("") : M + log2f(L);
+    const float lse2 = any_bad ? __builtin_nanf("") : mx + log2f(L);
     if (nsplit == 1) {
-      p.out[((size_t)b * p.num_q_heads + h0 + g) * D + d] = any_bad ? __builtin_nanf("") : o;
-      if (p.out_lse && d == 0) p.out_lse[(size_t)b * p.num_q_heads + h0 + g] = lse2 * kLn2;
+      p.out[row_index(g) * D + d] = any_bad ? __builtin_nanf("") : o;
+      if (p.out_lse && d == 0) p.out_lse[row_index(g)] = lse2 * kLn2;
     } else {
-      store_coherent(&p.ws_o[((prow + split) * G + g) * D + d], o);
-      if (d == 0) store_coherent(&p.ws_lse[(prow + split) * G + g], lse2);
+      store_coherent(&p.ws_o[((prow + split) * M + g) * D + d], o);
+      if (d == 0) store_coherent(&p.ws_lse[(prow + split) * M + g], lse2);
     }
   }
   if (nsplit == 1) return;
@@ -901,10 +922,15 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
 
   // Final merge.  The partial outputs do not depend on the split weights, so
   // the first batch of them is loaded before the weights are computed, and the
-  // weights' lse loads fly at the same time: one memory round trip.
+  // weights' lse loads fly at the same time: one memory round trip.  Partial
+  // rows are M apart; rows R..M-1 (padding when R is not a power of two) are
+  // combined like the others but never stored.
   const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-      p.ws_o + prow * G * D, 0, nsplit * G * D * 4, kBufferRsrcWord3);
-  float4* outp = reinterpret_cast<float4*>(p.out + ((size_t)b * p.num_q_heads + h0) * D);
+      p.ws_o + prow * M * D, 0, nsplit * M * D * 4, kBufferRsrcWord3);
+  auto store_out = [&](int c, const float4& o) {   // column c: row (4c)/D, dims 4(c % (D/4))..
+    const int m = (c * 4) / D;
+    if (m < R) *reinterpret_cast<float4*>(p.out + row_index(m) * D + (c * 4) % D) = o;
+  };
   const int part = NT >= C4 ? tid / C4 : 0;        // this thread's splits: part, part + SP, ...
   const int c0 = NT >= C4 ? tid % C4 : tid;        // first float4 column of this thread
   // loads in flight per thread: enough for all splits when a column has many
@@ -922,18 +948,18 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
   f32x4 v[MB];
   if (c0 < C4) load_batch(c0, part, v);
 
-  // Split weights per head: w_s = 2^(lse_s - M) / sum, one wave per head.
-  float* sm_w = sm_buf;                            // [G][64]
-  float* sm_lse = sm_buf + G * kWave;              // [G] merged base-2 lse
-  float4* sm_red = reinterpret_cast<float4*>(sm_buf + G * kWave + 4 * ((G + 3) / 4));
-  for (int g = wave; g < G; g += WAVES) {
-    const float x = lane < nsplit ? load_coherent(&p.ws_lse[(prow + lane) * G + g]) : kNegInf;
+  // Split weights per row: w_s = 2^(lse_s - max) / sum, one wave per row.
+  float* sm_w = sm_buf;                            // [M][64]
+  float* sm_lse = sm_buf + M * kWave;              // [M] merged base-2 lse
+  float4* sm_red = reinterpret_cast<float4*>(sm_buf + M * kWave + 4 * ((M + 3) / 4));
+  for (int g = wave; g < M; g += WAVES) {
+    const float x = lane < nsplit ? load_coherent(&p.ws_lse[(prow + lane) * M + g]) : kNegInf;
     const bool nan = __any(x != x);
-    const float M = class_max<1>(x);
-    const float w = lane < nsplit ? fast_exp2(x - M) : 0.f;
+    const float mx = class_max<1>(x);
+    const float w = lane < nsplit ? fast_exp2(x - mx) : 0.f;
     const float L = class_sum<1>(w);
     sm_w[g * kWave + lane] = nan ? __builtin_nanf("") : w / L;
-    if (lane == 0) sm_lse[g] = nan ? __builtin_nanf("") : M + log2f(L);
+    if (lane == 0) sm_lse[g] = nan ? __builtin_nanf("") : mx + log2f(L);
   }
   __syncthreads();
 
@@ -957,7 +983,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
       load_batch(c, sb, v);
     }
     if constexpr (SP > 1) sm_red[part * C4 + c] = o;
-    else outp[c] = o;
+    else store_out(c, o);
     if (c + (NT >= C4 ? C4 : NT) < C4) load_batch(c + (NT >= C4 ? C4 : NT), part, v);
   }
   if constexpr (SP > 1) {
@@ -969,10 +995,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_decode_kernel(DecodeParam
         const float4 v = sm_red[q * C4 + c];
         o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
       }
-      outp[c] = o;
+      store_out(c, o);
     }
   }
-  if (p.out_lse && tid < G) p.out_lse[(size_t)b * p.num_q_heads + h0 + tid] = sm_lse[tid] * kLn2;
+  if (p.out_lse && tid < R) p.out_lse[row_index(tid)] = sm_lse[tid] * kLn2;
   if (tid == 0)
     __hip_atomic_store(&p.counters[((size_t)b * p.num_kv_heads + kvh) * kCounterStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);

@@ -74,14 +74,24 @@ struct WorkspaceLayout {
   size_t o_off, lse_off, cnt_words, total;
 };
 
-// [counters: B*Hkv*kCounterStride u32][partial outputs: B*Hkv*S*G*D fp32]
-// [partial lse: B*Hkv*S*G fp32].  The counters come first so that a workspace
+// Rows per (sequence, KV head): G * Q, rounded up to a power of two (the
+// kernel's row capacity M).
+int row_capacity(int rows) {
+  int m = 1;
+  while (m < rows) m <<= 1;
+  return m;
+}
+
+// [counters: B*Hkv*kCounterStride u32][partial outputs: B*Hkv*S*M*D fp32]
+// [partial lse: B*Hkv*S*M fp32].  The counters come first so that a workspace
 // initialised for one shape serves any later call with no more (sequence, KV
 // head) pairs.
-WorkspaceLayout workspace_layout(const gqa_paged_shape* s, int max_splits) {
+WorkspaceLayout workspace_layout(const gqa_paged_shape* s, int max_splits, int num_queries) {
   WorkspaceLayout w;
   w.cnt_words = (size_t)s->num_seqs * s->num_kv_heads * gqa::kCounterStride;
-  const size_t rows = (size_t)s->num_seqs * s->num_q_heads * (size_t)max_splits;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const size_t rows = (size_t)s->num_seqs * s->num_kv_heads *
+                      (size_t)row_capacity(G * num_queries) * (size_t)max_splits;
   w.o_off = (w.cnt_words * sizeof(uint32_t) + 255) & ~size_t(255);
   w.lse_off = (w.o_off + rows * s->head_dim * sizeof(float) + 255) & ~size_t(255);
   w.total = w.lse_off + rows * sizeof(float);
@@ -93,34 +103,46 @@ int max_splits_for(int32_t max_context_len) {
   return ms < 1 ? 1 : ms;
 }
 
-// Kernel dispatch over the supported (D, BS, G, dtype, waves) combinations.
-template <int D, int BS, int G, int W>
-const void* pick_kernel_g(bool fp8) {
-  return fp8 ? reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, true, W>)
-             : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, G, false, W>);
+// Kernel dispatch over the supported (D, BS, rows M, dtype, waves) combinations.
+// M is the row capacity, the power of two at or above G * Q: up to 16 on the
+// matrix path (bf16), up to 8 on the vector path (fp8).
+constexpr int kMaxRowsBf16 = 16;
+constexpr int kMaxRowsFp8 = 8;
+
+template <int D, int BS, int M, int W>
+const void* pick_kernel_m(bool fp8) {
+  if constexpr (M > kMaxRowsFp8) {
+    return fp8 ? nullptr
+               : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, false, W>);
+  } else {
+    return fp8 ? reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, true, W>)
+               : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, false, W>);
+  }
 }
 
 template <int D, int BS, int W>
-const void* pick_kernel_bs(int G, bool fp8) {
-  switch (G) {
-    case 1: return pick_kernel_g<D, BS, 1, W>(fp8);
-    case 2: return pick_kernel_g<D, BS, 2, W>(fp8);
-    case 4: return pick_kernel_g<D, BS, 4, W>(fp8);
-    case 8: return pick_kernel_g<D, BS, 8, W>(fp8);
+const void* pick_kernel_bs(int M, bool fp8) {
+  switch (M) {
+    case 1: return pick_kernel_m<D, BS, 1, W>(fp8);
+    case 2: return pick_kernel_m<D, BS, 2, W>(fp8);
+    case 4: return pick_kernel_m<D, BS, 4, W>(fp8);
+    case 8: return pick_kernel_m<D, BS, 8, W>(fp8);
+    case 16: return pick_kernel_m<D, BS, 16, W>(fp8);
   }
   return nullptr;
 }
 
 template <int W>
-const void* pick_kernel_w(int D, int BS, int G, bool fp8) {
+const void* pick_kernel_w(int D, int BS, int M, bool fp8) {
   if (D == 64)
-    return BS == 16 ? pick_kernel_bs<64, 16, W>(G, fp8) : pick_kernel_bs<64, 32, W>(G, fp8);
-  return BS == 16 ? pick_kernel_bs<128, 16, W>(G, fp8) : pick_kernel_bs<128, 32, W>(G, fp8);
+    return BS == 16 ? pick_kernel_bs<64, 16, W>(M, fp8) : pick_kernel_bs<64, 32, W>(M, fp8);
+  return BS == 16 ? pick_kernel_bs<128, 16, W>(M, fp8) : pick_kernel_bs<128, 32, W>(M, fp8);
 }
 
-const void* pick_kernel(int D, int BS, int G, bool fp8, int waves) {
-  return waves == 8 ? pick_kernel_w<8>(D, BS, G, fp8) : pick_kernel_w<4>(D, BS, G, fp8);
+const void* pick_kernel(int D, int BS, int M, bool fp8, int waves) {
+  return waves == 8 ? pick_kernel_w<8>(D, BS, M, fp8) : pick_kernel_w<4>(D, BS, M, fp8);
 }
+
 
 // Waves per workgroup.  An eight-wave workgroup covers twice the tokens of a
 // four-wave one at the same number of resident waves (one per CU instead of
@@ -181,7 +203,7 @@ extern "C" {
 
 const char* gqa_last_error(void) { return g_last_error.c_str(); }
 
-const char* gqa_version(void) { return "gqa_paged 0.2 (gfx950)"; }
+const char* gqa_version(void) { return "gqa_paged 0.3 (gfx950)"; }
 
 int32_t gqa_decode_num_splits(int32_t context_len) {
   return gqa::split_plan(context_len).num_splits;
@@ -189,17 +211,26 @@ int32_t gqa_decode_num_splits(int32_t context_len) {
 
 size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max_context_len) {
   if (check_shape(shape) != GQA_OK || max_context_len < 0) return 0;
-  return workspace_layout(shape, max_splits_for(max_context_len)).total;
+  return workspace_layout(shape, max_splits_for(max_context_len), 1).total;
 }
 
-gqa_status gqa_kv_append(const gqa_paged_shape* s, const void* k_new, const void* v_new,
-                         void* k_cache, void* v_cache, const int32_t* block_tables,
-                         const int32_t* positions, hipStream_t stream) {
+size_t gqa_paged_multi_query_workspace_size(const gqa_paged_shape* shape, int32_t num_queries,
+                                            int32_t max_context_len) {
+  if (check_shape(shape) != GQA_OK || max_context_len < 0 || num_queries < 1) return 0;
+  return workspace_layout(shape, max_splits_for(max_context_len), num_queries).total;
+}
+
+static gqa_status append_impl(const gqa_paged_shape* s, int32_t num_tokens, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* positions,
+                              hipStream_t stream) {
   gqa_status st = check_shape(s);
   if (st != GQA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535)
+    return fail(GQA_ERR_INVALID_ARG, "num_tokens %d outside [0, 65535]", num_tokens);
   if (s->kv_dtype != GQA_KV_BF16)
     return fail(GQA_ERR_UNSUPPORTED, "kv_append supports bf16 pools only");
-  if (s->num_seqs == 0) return ok();
+  if (s->num_seqs == 0 || num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !positions)
     return fail(GQA_ERR_INVALID_ARG, "kv_append: NULL device pointer");
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -211,17 +242,33 @@ gqa_status gqa_kv_append(const gqa_paged_shape* s, const void* k_new, const void
   p.v_cache = static_cast<uint16_t*>(v_cache);
   p.block_tables = block_tables;
   p.positions = positions;
+  p.num_tokens = num_tokens;
   p.num_kv_heads = s->num_kv_heads;
   p.head_dim = s->head_dim;
   p.block_size = s->block_size;
   p.num_blocks = s->num_blocks;
   p.max_blocks = s->max_blocks_per_seq;
-  st = launch(reinterpret_cast<const void*>(&gqa::kv_append_kernel), dim3(s->num_seqs),
-              dim3(256), &p, "kv_append", stream);
+  st = launch(reinterpret_cast<const void*>(&gqa::kv_append_kernel),
+              dim3(s->num_seqs, num_tokens), dim3(256), &p, "kv_append", stream);
   return st == GQA_OK ? ok() : st;
 }
 
-static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_cache,
+gqa_status gqa_kv_append(const gqa_paged_shape* s, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                         const int32_t* positions, hipStream_t stream) {
+  return append_impl(s, 1, k_new, v_new, k_cache, v_cache, block_tables, positions, stream);
+}
+
+gqa_status gqa_kv_append_tokens(const gqa_paged_shape* s, int32_t num_tokens, const void* k_new,
+                                const void* v_new, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, const int32_t* positions,
+                                hipStream_t stream) {
+  return append_impl(s, num_tokens, k_new, v_new, k_cache, v_cache, block_tables, positions,
+                     stream);
+}
+
+static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, const void* q,
+                              void* k_cache,
                               void* v_cache, const float* k_scale, const float* v_scale,
                               const void* k_new, const void* v_new, const int32_t* positions,
                               const int32_t* block_tables, const int32_t* context_lens,
@@ -244,6 +291,12 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
   if (positions && fp8)
     return fail(GQA_ERR_UNSUPPORTED, "the fused append supports bf16 pools only");
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (num_queries < 1) return fail(GQA_ERR_INVALID_ARG, "num_queries %d < 1", num_queries);
+  if ((int64_t)G * num_queries > (fp8 ? kMaxRowsFp8 : kMaxRowsBf16))
+    return fail(GQA_ERR_UNSUPPORTED, "G * num_queries = %lld rows exceeds %d for this KV dtype",
+                (long long)G * num_queries, fp8 ? kMaxRowsFp8 : kMaxRowsBf16);
+  const int rows = G * num_queries;
   if (s->num_seqs == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(GQA_ERR_INVALID_ARG, "decode: NULL device pointer");
@@ -252,15 +305,14 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
     return fail(GQA_ERR_INVALID_ARG, "decode: q, caches, new rows and out must be 16-byte aligned");
-  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len));
+  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len), num_queries);
   if (!workspace || workspace_bytes < wl.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 wl.total);
   if (!aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  const int G = s->num_q_heads / s->num_kv_heads;
   const int waves = pick_waves(s);
-  const void* fn = pick_kernel(s->head_dim, s->block_size, G, fp8, waves);
+  const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows), fp8, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
   const int target = target_splits(s, fn, waves * 64);
   int launch_splits = gqa::split_plan(max_context_len, target).num_splits;
@@ -292,6 +344,10 @@ static gqa_status decode_impl(const gqa_paged_shape* s, const void* q, void* k_c
   p.counters = reinterpret_cast<uint32_t*>(ws);
   p.num_q_heads = s->num_q_heads;
   p.num_kv_heads = s->num_kv_heads;
+  p.group = G;
+  p.group_shift = __builtin_ctz((unsigned)G);
+  p.num_queries = num_queries;
+  p.rows = rows;
   p.num_blocks = s->num_blocks;
   p.max_blocks = s->max_blocks_per_seq;
   p.max_splits = max_splits_for(max_context_len);
@@ -311,8 +367,21 @@ gqa_status gqa_paged_decode_attention(const gqa_paged_shape* s, const void* q,
                                       int32_t max_context_len, float softmax_scale, float* out,
                                       float* out_lse, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream) {
-  return decode_impl(s, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_scale,
+  return decode_impl(s, 1, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_scale,
                      v_scale, nullptr, nullptr, nullptr, block_tables, context_lens,
+                     max_context_len, softmax_scale, out, out_lse, workspace, workspace_bytes,
+                     stream);
+}
+
+gqa_status gqa_paged_decode_multi_query(const gqa_paged_shape* s, int32_t num_queries,
+                                        const void* q, const void* k_cache, const void* v_cache,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        int32_t max_context_len, float softmax_scale, float* out,
+                                        float* out_lse, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  return decode_impl(s, num_queries, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                     k_scale, v_scale, nullptr, nullptr, nullptr, block_tables, context_lens,
                      max_context_len, softmax_scale, out, out_lse, workspace, workspace_bytes,
                      stream);
 }
@@ -324,7 +393,7 @@ gqa_status gqa_paged_decode_append_attention(
     float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (s && s->num_seqs > 0 && !positions)
     return fail(GQA_ERR_INVALID_ARG, "append: NULL positions");
-  return decode_impl(s, q, k_cache, v_cache, nullptr, nullptr, k_new, v_new, positions,
+  return decode_impl(s, 1, q, k_cache, v_cache, nullptr, nullptr, k_new, v_new, positions,
                      block_tables, context_lens, max_context_len, softmax_scale, out, out_lse,
                      workspace, workspace_bytes, stream);
 }
@@ -336,10 +405,10 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* s, int32_t max
   if (st != GQA_OK) return st;
   if (max_context_len < 0)
     return fail(GQA_ERR_INVALID_ARG, "max_context_len %d < 0", max_context_len);
-  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len));
-  if (!workspace || workspace_bytes < wl.total)
+  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len), 1);
+  if (!workspace || workspace_bytes < wl.cnt_words * sizeof(uint32_t))
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
-                wl.total);
+                wl.cnt_words * sizeof(uint32_t));
   if (wl.cnt_words == 0) return ok();
   uint32_t* cnt = static_cast<uint32_t*>(workspace);
   size_t n = wl.cnt_words;

@@ -1,4 +1,4 @@
-// KV append (commit one new token per sequence) and a block-table gather.
+// KV append (commit new tokens of each sequence) and a block-table gather.
 //
 // Cites: *LLM Inference Systems Engineering* (jasonzhang109) §2.1.3 — a decode
 // step first writes the pending token's K/V into the cache, then attends;
@@ -15,12 +15,13 @@
 namespace gqa {
 
 struct AppendParams {
-  const uint16_t* k_new;        // [B][Hkv][D]
+  const uint16_t* k_new;        // [B][T][Hkv][D]
   const uint16_t* v_new;
   uint16_t* k_cache;            // [NB][Hkv][BS][D]
   uint16_t* v_cache;
   const int32_t* block_tables;  // [B][max_blocks]
-  const int32_t* positions;     // [B]
+  const int32_t* positions;     // [B][T]; a position outside [0, max_blocks*BS) is skipped
+  int32_t num_tokens;           // T
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
@@ -28,10 +29,12 @@ struct AppendParams {
   int32_t max_blocks;
 };
 
-// grid: B workgroups; each thread copies 16 B units of the K and V rows.
+// grid: (B, T) workgroups, one per new token; each thread copies 16 B units of
+// the token's K and V rows.
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int b = blockIdx.x;
-  const int pos = p.positions[b];
+  const size_t tok = (size_t)b * p.num_tokens + blockIdx.y;   // row of k_new / positions
+  const int pos = p.positions[tok];
   if (pos < 0 || pos >= p.max_blocks * p.block_size) return;
   const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / p.block_size];
   if (blk < 0 || blk >= p.num_blocks) return;
@@ -40,7 +43,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   for (int u = threadIdx.x; u < p.num_kv_heads * upr; u += blockDim.x) {
     const int h = u / upr;
     const int c = u % upr;
-    const size_t src = ((size_t)b * p.num_kv_heads + h) * p.head_dim + c * 8;
+    const size_t src = (tok * p.num_kv_heads + h) * p.head_dim + c * 8;
     const size_t dst = (((size_t)blk * p.num_kv_heads + h) * p.block_size + slot) * p.head_dim + c * 8;
     *reinterpret_cast<uint4*>(p.k_cache + dst) = *reinterpret_cast<const uint4*>(p.k_new + src);
     *reinterpret_cast<uint4*>(p.v_cache + dst) = *reinterpret_cast<const uint4*>(p.v_new + src);

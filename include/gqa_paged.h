@@ -1,8 +1,10 @@
 /*
  * gqa_paged.h — C ABI of the MI355X (gfx950) paged GQA decode-attention library.
  *
- * The library computes single-token decode attention over a paged KV cache with
- * grouped query heads, and the KV append that commits a new token before it.
+ * The library computes decode attention over a paged KV cache with grouped
+ * query heads (one query position per sequence, or a few consecutive ones, as
+ * when verifying speculative tokens), and the KV append that commits new
+ * tokens before it.
  *
  * What the operations are, and where the pages state them:
  *  - KV cache and append: each step commits the pending token's K/V, then its
@@ -23,6 +25,11 @@
  *  - FP8 KV: E4M3 in the finite-only convention (max 448), dequantised inside the
  *    kernel with a scale.  *Module 10*, number-format table; *The Mathematics of
  *    Transformer Inference* §11.
+ *  - Several query positions per sequence: speculative decoding verifies k
+ *    drafted tokens with one target pass over the committed prefix plus those
+ *    positions, each attending causally.  *LLM Inference Systems Engineering*
+ *    §2.1.3 (the verification interface); *The Mathematics of Transformer
+ *    Inference* §10.
  *
  * Conventions shared by all calls
  *  - All pointers except `shape` are DEVICE pointers on the current HIP device,
@@ -115,6 +122,23 @@ gqa_status gqa_kv_append(const gqa_paged_shape* shape,
                          hipStream_t stream);
 
 /*
+ * gqa_kv_append_tokens — commit num_tokens new tokens per sequence (for
+ * example a pending token and its drafts before verification).
+ *   num_tokens    T in [0, 65535]
+ *   k_new, v_new  [B][T][H_kv][d_h] bf16 rows
+ *   positions     [B][T] int32 logical slots; a position outside
+ *                 [0, max_blocks_per_seq * block_size) skips that token
+ *   other arguments as gqa_kv_append, which is the T = 1 case.  Tokens are
+ *   copied independently (bit-exact); two tokens given the same slot leave
+ *   either one there.  bf16 pools only.
+ */
+gqa_status gqa_kv_append_tokens(const gqa_paged_shape* shape, int32_t num_tokens,
+                                const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache,
+                                const int32_t* block_tables, const int32_t* positions,
+                                hipStream_t stream);
+
+/*
  * gqa_decode_num_splits — the batch-invariant context split plan (host
  * function, no GPU): how many partial attentions a sequence of `context_len`
  * tokens is cut into under GQA_FLAG_BATCH_INVARIANT, which is also the most
@@ -172,6 +196,47 @@ gqa_status gqa_paged_decode_attention(const gqa_paged_shape* shape,
                                       hipStream_t stream);
 
 /*
+ * gqa_paged_multi_query_workspace_size — workspace bytes for
+ * gqa_paged_decode_multi_query with num_queries positions per sequence (equal
+ * to gqa_paged_decode_workspace_size when num_queries is 1).  0 for invalid
+ * arguments.
+ */
+size_t gqa_paged_multi_query_workspace_size(const gqa_paged_shape* shape, int32_t num_queries,
+                                            int32_t max_context_len);
+
+/*
+ * gqa_paged_decode_multi_query — attention for Q consecutive query positions
+ * per sequence over the paged cache, as in the verification pass of
+ * speculative decoding or a short chunk of prefill onto a cache.
+ *   num_queries   Q >= 1, with G * Q <= 16 for bf16 pools and <= 8 for fp8
+ *                 (else GQA_ERR_UNSUPPORTED)
+ *   q             [B][Q][H_q][d_h] bf16; query i of sequence b sits at position
+ *                 context_lens[b] - Q + i, so the Q new tokens must already be
+ *                 in the cache (gqa_kv_append_tokens)
+ *   context_lens  [B] int32 tokens in the cache including the Q new ones.
+ *                 Query i attends to tokens 0 .. context_lens[b] - Q + i
+ *                 (causal among the new positions).  0 gives out = 0 and
+ *                 lse = -inf; 0 < context_lens[b] < Q gives NaN.
+ *   out           [B][Q][H_q][d_h] fp32; out_lse [B][Q][H_q] fp32 or NULL
+ *   workspace     at least gqa_paged_multi_query_workspace_size(shape,
+ *                 num_queries, max_context_len) bytes, counters as described
+ *                 for gqa_paged_decode_attention
+ *   other arguments as gqa_paged_decode_attention, which is the Q = 1 case
+ *   (same kernel, same bits).
+ */
+gqa_status gqa_paged_decode_multi_query(const gqa_paged_shape* shape, int32_t num_queries,
+                                        const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* block_tables,
+                                        const int32_t* context_lens,
+                                        int32_t max_context_len,
+                                        float softmax_scale,
+                                        float* out, float* out_lse,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/*
  * gqa_paged_decode_append_attention — one fused decode step ("forward and
  * commit"): write each sequence's new token into the cache, then attend over
  * context_lens[b] tokens that include it, in a single kernel.
@@ -198,9 +263,9 @@ gqa_status gqa_paged_decode_append_attention(const gqa_paged_shape* shape,
 
 /*
  * gqa_paged_decode_workspace_init — zero the arrival counters (the first
- * B*H_kv*64 words) of a workspace sized for (shape, max_context_len).  Enqueued on
+ * B*H_kv*64 words) of a workspace; workspace_bytes must cover them.  Enqueued on
  * `stream` as a small fill kernel (no memset), so it may be captured in a HIP
- * graph.
+ * graph.  max_context_len is validated but does not change what is zeroed.
  */
 gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t max_context_len,
                                            void* workspace, size_t workspace_bytes,

@@ -1,0 +1,129 @@
+"""GPU parity of multi-position queries (speculative verification): the new
+tokens are committed with gqa_kv_append_tokens, then gqa_paged_decode_multi_query
+attends for every query position, compared with the float64 oracle.  Same bar
+as the single-query path: max-abs <= 1e-2, relative L2 <= 2e-3, lse within 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._dev import to_device, assert_parity
+from workloads import make_multi_query_case, small_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def _reference(case):
+    s = case["spec"]
+    return oracle.paged_multi_query_attention(case["q"], case["k_pool_full"], case["v_pool_full"],
+                                              case["block_tables"], case["context_lens"],
+                                              s.block_size, case["softmax_scale"], s.kv_dtype,
+                                              case["k_scale"], case["v_scale"])
+
+
+def _verify_step(gqa, case, dev, max_context_len=None, batch_invariant=False):
+    """Commit the Q new tokens (bf16 pools), then attend for all Q positions."""
+    if case["k_new"] is not None:
+        gqa.kv_append_tokens(dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                             dev["block_tables"], dev["positions"])
+    if max_context_len is None:
+        max_context_len = int(case["context_lens"].max())
+    out, lse = gqa.paged_decode_multi_query(dev["q"], dev["k_cache"], dev["v_cache"],
+                                            dev["block_tables"], dev["context_lens"],
+                                            max_context_len, case["softmax_scale"],
+                                            dev["k_scale"], dev["v_scale"],
+                                            batch_invariant=batch_invariant)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("hq,hkv,nq,d,bs,dt", [
+    (32, 8, 4, 128, 16, "bf16"),     # G=4, 4 positions: 16 rows, a full MFMA tile
+    (64, 8, 2, 128, 32, "bf16"),     # G=8, 2 positions
+    (8, 8, 16, 128, 16, "bf16"),     # MHA, 16 positions
+    (16, 8, 3, 64, 16, "bf16"),      # 6 rows in an 8-row tile
+    (32, 8, 3, 128, 16, "bf16"),     # 12 rows in a 16-row tile
+    (8, 8, 1, 128, 32, "bf16"),      # one row: the vector path
+    (4, 4, 2, 128, 16, "fp8"),
+    (16, 4, 2, 64, 32, "fp8"),
+    (8, 8, 8, 128, 16, "fp8"),
+])
+def test_multi_query_parity(gpu, hq, hkv, nq, d, bs, dt):
+    lens = [nq, nq + 1, 100, 1000, 3000]
+    spec = small_spec(num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      block_size=bs, kv_dtype=dt, context=3000, case_id=6000 + hq * 10 + nq)
+    case = make_multi_query_case(spec, nq, seed=3, context_lens=lens, append=(dt == "bf16"))
+    ref, ref_lse = _reference(case)
+    dev = to_device(case)
+    out, lse = _verify_step(gpu, case, dev)
+    assert_parity(out, lse, ref, ref_lse, f"G={hq // hkv} Q={nq} d={d} bs={bs} {dt}")
+    if dt == "bf16":
+        k = dev["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(k, case["k_pool_full"])
+
+
+def test_single_position_matches_the_decode_entry_point_bitwise(gpu):
+    spec = small_spec(num_seqs=3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context=2000, case_id=6100)
+    case = make_multi_query_case(spec, 1, seed=4, context_lens=[2000, 700, 33], append=False)
+    dev = to_device(case)
+    o1, l1 = gpu.paged_decode_multi_query(dev["q"], dev["k_cache"], dev["v_cache"],
+                                          dev["block_tables"], dev["context_lens"], 2000)
+    o2, l2 = gpu.paged_decode_attention(dev["q"][:, 0].contiguous(), dev["k_cache"],
+                                        dev["v_cache"], dev["block_tables"],
+                                        dev["context_lens"], 2000)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, 0], o2) and torch.equal(l1[:, 0], l2)
+
+
+def test_malformed_and_empty_contexts(gpu):
+    spec = small_spec(num_seqs=4, num_q_heads=16, num_kv_heads=4, head_dim=64, block_size=16,
+                      context=300, case_id=6200)
+    case = make_multi_query_case(spec, 4, seed=5, context_lens=[300, 2, 0, 4], append=False)
+    ref, ref_lse = _reference(case)
+    out, lse = _verify_step(gpu, case, to_device(case))
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(lse[1]))
+    assert np.all(out[2] == 0) and np.all(lse[2] == -np.inf)
+    keep = [0, 3]
+    assert_parity(out[keep], lse[keep], ref[keep], ref_lse[keep], "valid sequences")
+
+
+@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 5, "bf16"), (16, 8, 5, "fp8")])
+def test_too_many_rows_is_unsupported(gpu, hq, hkv, nq, dt):
+    spec = small_spec(num_seqs=1, num_q_heads=hq, num_kv_heads=hkv, head_dim=64, block_size=16,
+                      kv_dtype=dt, context=64, case_id=6300)
+    case = make_multi_query_case(spec, nq, seed=6, append=False)
+    dev = to_device(case)
+    with pytest.raises(gpu.GqaError) as e:
+        gpu.paged_decode_multi_query(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                     dev["context_lens"], 64, None, dev["k_scale"], dev["v_scale"])
+    assert e.value.status == 2
+
+
+def test_batch_invariant_mode(gpu):
+    """With the flag, each sequence's bits do not depend on the rest of the batch."""
+    spec = small_spec(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context=5000, case_id=6400)
+    case = make_multi_query_case(spec, 4, seed=7, context_lens=[5000, 64, 1500, 4096],
+                                 append=False)
+    ref, ref_lse = _reference(case)
+    hint = case["block_tables"].shape[1] * 16
+    out, lse = _verify_step(gpu, case, to_device(case), max_context_len=hint,
+                            batch_invariant=True)
+    assert_parity(out, lse, ref, ref_lse, "batch-invariant")
+    one = dict(case)
+    for key in ("q", "block_tables", "context_lens", "positions"):
+        one[key] = case[key][2:3]
+    o1, l1 = _verify_step(gpu, one, to_device(one), batch_invariant=True)
+    assert np.array_equal(o1[0], out[2]) and np.array_equal(l1[0], lse[2])
+
+
+def test_speculative_verify_full_size(gpu):
+    """The 8K grouped-query shape (B=1, 32/8 heads, d=128) verifying 3 drafts plus the
+    pending token: 4 positions appended, then attended."""
+    spec = small_spec(num_seqs=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context=8192, case_id=6500)
+    case = make_multi_query_case(spec, 4, seed=8)
+    ref, ref_lse = _reference(case)
+    out, lse = _verify_step(gpu, case, to_device(case))
+    assert_parity(out, lse, ref, ref_lse, "verify 8K")
