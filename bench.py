@@ -12,6 +12,10 @@ rather than the 256 MB on-die Infinity Cache, consecutive steps rotate over
 enough copies of the KV pool that each step's KV bytes were last touched at
 least 1 GiB of other KV reads ago.
 
+Workload ``verify4`` is the verification pass of speculative decoding on the
+8K grouped-query shape: each step commits 4 new tokens (the pending one and 3
+drafts) and attends for all 4 positions, in one fused kernel.
+
 Prints one JSON line (rank 0, N=1).  `value` = algorithmic KV bytes per step /
 step time.  `roofline.achieved` = the same bytes / the decode-attention call's
 average duration measured with HIP events on the launch stream.  The float64
@@ -124,13 +128,14 @@ def cpu_baseline(case, kv_bytes, min_seconds):
     from threadpoolctl import threadpool_limits
     import oracle
     spec = case["spec"]
+    fn = (oracle.paged_multi_query_attention if case.get("num_queries")
+          else oracle.paged_decode_attention)
     n, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
         while True:
-            oracle.paged_decode_attention(case["q"], case["k_pool_full"], case["v_pool_full"],
-                                          case["block_tables"], case["context_lens"],
-                                          spec.block_size, case["softmax_scale"], spec.kv_dtype,
-                                          case["k_scale"], case["v_scale"])
+            fn(case["q"], case["k_pool_full"], case["v_pool_full"], case["block_tables"],
+               case["context_lens"], spec.block_size, case["softmax_scale"], spec.kv_dtype,
+               case["k_scale"], case["v_scale"])
             n += 1
             el = time.perf_counter() - t0
             if el >= min_seconds:
@@ -138,7 +143,9 @@ def cpu_baseline(case, kv_bytes, min_seconds):
     per_step = el / n
     return {"value": round(kv_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{n} whole step(s) of the {spec.name} workload, float64 numpy oracle, "
+            "sample": f"{n} whole step(s) of the {spec.name} workload"
+                      f"{' with %d query positions' % case['num_queries'] if case.get('num_queries') else ''}"
+                      ", float64 numpy oracle, "
                       f"1 BLAS thread, {el:.1f} s total ({per_step * 1e3:.1f} ms/step)"}
 
 
@@ -148,7 +155,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b",
-                    choices=["tiny", "llama8b", "batched", "long", "mha_fp8"])
+                    choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -168,17 +175,18 @@ def main():
 
     import numpy as np
 
+    verify = args.workload == "verify4"          # 4 query positions on the 8K shape
     if args.traffic_from:
         from workloads import make_case, SPECS
-        spec = SPECS[args.workload]
-        write_traffic(spec.name, args.traffic_from,
+        spec = SPECS["llama8b" if verify else args.workload]
+        write_traffic(args.workload, args.traffic_from,
                       kv_bytes_per_step(spec, make_case(spec, seed=args.seed)["context_lens"]))
         return
 
     import torch
 
     import gqa_decode_attention_paged_amd as gqa
-    from workloads import make_case, SPECS
+    from workloads import make_case, make_multi_query_case, SPECS
 
     if args.copy_calibration:
         # A plain elementwise kernel that reads and writes COPY_BYTES each: the known
@@ -193,8 +201,10 @@ def main():
 
     gqa.load()
     dev = torch.device("cuda:0")
-    spec = SPECS[args.workload]
-    case = make_case(spec, seed=args.seed)
+    spec = SPECS["llama8b" if verify else args.workload]
+    case = (make_multi_query_case(spec, 4, seed=args.seed) if verify
+            else make_case(spec, seed=args.seed))
+    nq = case.get("num_queries", 1)
     kv_bytes = kv_bytes_per_step(spec, case["context_lens"])
 
     def bf16(a):
@@ -216,14 +226,19 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     max_ctx = int(case["context_lens"].max())
     shape = gqa.make_shape(spec.num_seqs, spec.num_q_heads, k0, bt)
-    ws = gqa.make_workspace(shape, max_ctx, dev)
-    out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
-    lse = torch.empty((spec.num_seqs, spec.num_q_heads), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(16, gqa.multi_query_workspace_size(shape, nq, max_ctx)),
+                     dtype=torch.uint8, device=dev)
+    rows = (spec.num_seqs, nq, spec.num_q_heads) if verify else (spec.num_seqs, spec.num_q_heads)
+    out = torch.empty(rows + (spec.head_dim,), dtype=torch.float32, device=dev)
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
     scale = case["softmax_scale"]
 
     def step(i):
         kc, vc = pools[i % copies]
-        if k_new is not None:      # fused: commit the new token and attend, one kernel
+        if verify:                 # fused: commit the 4 new tokens, attend for all 4 positions
+            gqa.paged_decode_multi_query_append(q, k_new, v_new, kc, vc, bt, ctx, max_ctx, scale,
+                                                out=out, out_lse=lse, workspace=ws)
+        elif k_new is not None:    # fused: commit the new token and attend, one kernel
             gqa.paged_decode_append_attention(q, k_new, v_new, pos, kc, vc, bt, ctx, max_ctx,
                                               scale, out=out, out_lse=lse, workspace=ws)
         else:
@@ -266,8 +281,13 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     call_ms = gpu_ms / args.steps
     achieved = kv_bytes / (call_ms * 1e-3) / 1e9
-    kernel = ("paged_decode_kernel (fused KV append + split attention + log-sum-exp merge)"
-              if k_new is not None else "paged_decode_kernel (split attention + log-sum-exp merge)")
+    if verify:
+        kernel = ("paged_decode_kernel (fused 4-token KV append + 4 query positions, split "
+                  "attention + log-sum-exp merge)")
+    elif k_new is not None:
+        kernel = "paged_decode_kernel (fused KV append + split attention + log-sum-exp merge)"
+    else:
+        kernel = "paged_decode_kernel (split attention + log-sum-exp merge)"
 
     result = {
         "metric": METRIC,
@@ -284,10 +304,11 @@ def main():
         "dtype": "bf16" if spec.kv_dtype == "bf16" else "fp8",
         "data": "synthetic (seeded N(0,1) q/k/v, random block placement; no weights)",
         "config": {
-            "workload": spec.name, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
+            "workload": args.workload, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
             "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
             "block_size": spec.block_size, "kv_dtype": spec.kv_dtype,
             "context_lens_total": int(case["context_lens"].sum()), "append": spec.append,
+            "query_positions": nq,
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
         },
         "roofline": {
@@ -296,7 +317,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": counted_traffic(spec.name),
+            "traffic": counted_traffic(args.workload),
             "kernel": kernel,
             "kernel_us_events": round(call_ms * 1e3, 3),
             "timing": ("HIP events on the launch stream around one replay of a graph of the "

@@ -73,6 +73,10 @@ def load():
                                                  ctypes.c_int32, ctypes.c_float, _P, _P, _P,
                                                  ctypes.c_size_t, _P]
     lib.gqa_paged_decode_multi_query.restype = ctypes.c_int
+    lib.gqa_paged_decode_multi_query_append.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                                        _P, _P, ctypes.c_int32, ctypes.c_float,
+                                                        _P, _P, _P, ctypes.c_size_t, _P]
+    lib.gqa_paged_decode_multi_query_append.restype = ctypes.c_int
     lib.gqa_decode_num_splits.argtypes = [ctypes.c_int32]
     lib.gqa_decode_num_splits.restype = ctypes.c_int32
     lib.gqa_paged_decode_workspace_size.argtypes = [S, ctypes.c_int32]
@@ -212,6 +216,33 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
     _check(lib.gqa_paged_decode_attention(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, out_lse
+
+
+def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tables,
+                                    context_lens, max_context_len, softmax_scale=None, out=None,
+                                    out_lse=None, workspace=None, return_lse=True,
+                                    batch_invariant=False):
+    """Fused verification step: commit k_new/v_new [B][Q][H_kv][d_h] at positions
+    context_lens[b] - Q + i, then attend for the Q positions (one kernel)."""
+    import torch
+    lib = load()
+    B, Q, Hq, D = q.shape
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Q, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = multi_query_workspace_size(shape, Q, max_context_len)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.gqa_paged_decode_multi_query_append(
+        ctypes.byref(shape), int(Q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
         float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q)))
     return out, out_lse

@@ -67,9 +67,10 @@ struct DecodeParams {
   const float* v_scale;
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* context_lens;  // [B]
-  const uint16_t* k_new;        // [B][Hkv][D] fused append, or null
-  const uint16_t* v_new;
+  const uint16_t* k_new;        // fused append rows: [B][Hkv][D], or [B][Q][Hkv][D] with
+  const uint16_t* v_new;        //   append_tail; else null
   const int32_t* positions;     // [B] slot of the appended token, or null
+  int32_t append_tail;          // 1: commit k_new/v_new row i at position ctx - Q + i
   float* out;                   // [B][Q][Hq][D]
   float* out_lse;               // [B][Q][Hq] or null
   float* ws_o;                  // [B][Hkv][max_splits][M][D] partial outputs (normalised)
@@ -150,6 +151,7 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicySc1 = 16;         // buffer instruction cache-policy bit "sc1"
 constexpr int kBufferRsrcWord3 = 0x00020000;  // raw 32-bit buffer resource (gfx9 family)
 
@@ -416,26 +418,32 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   if (split >= nsplit) return;
   const int s0 = split * plan.split_tokens;
   const int s1 = min(ctx, s0 + plan.split_tokens);
-  const int app = (pos >= s0 && pos < s1) ? pos : -1;    // appended token of this split
   const int my_n = wave_chunks(s0, s1);
-  if (app >= 0) {
-    // The wave whose chunk holds the new token commits its K/V rows and waits
-    // for the stores, so its loads then read the token back from the cache.
-    const int c_app = (app - s0) / CT;
-    if (c_app % WAVES == wave) {
-      if (row == 0) {
-        const size_t src = ((size_t)b * p.num_kv_heads + kvh) * D + col * 8;
-        const int blk = bt[app / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks) {
-          const size_t dst = (((size_t)blk * p.num_kv_heads + kvh) * BS + app % BS) * D + col * 8;
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + dst) =
-              *reinterpret_cast<const uint4*>(p.k_new + src);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + dst) =
-              *reinterpret_cast<const uint4*>(p.v_new + src);
-        }
+  // Fused append: the token at `pos`, or with append_tail the Q query positions
+  // ctx-Q .. ctx-1 (row i of k_new/v_new).  The wave whose chunk holds a new
+  // token commits its K/V rows and waits for the stores, so its loads then read
+  // the token back from the cache.
+  {
+    const int na = p.append_tail ? Q : (pos >= 0 ? 1 : 0);
+    const int a0 = p.append_tail ? ctx - Q : pos;
+    bool wrote = false;
+    for (int i = 0; i < na; ++i) {
+      const int ap = a0 + i;
+      if (ap < s0 || ap >= s1 || ((ap - s0) / CT) % WAVES != wave) continue;
+      wrote = true;
+      if (row != 0) continue;
+      const size_t src = (((size_t)b * (p.append_tail ? Q : 1) + i) * p.num_kv_heads + kvh) * D +
+                         col * 8;
+      const int blk = bt[ap / BS];
+      if ((unsigned)blk < (unsigned)p.num_blocks) {
+        const size_t dst = (((size_t)blk * p.num_kv_heads + kvh) * BS + ap % BS) * D + col * 8;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + dst) =
+            *reinterpret_cast<const uint4*>(p.k_new + src);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + dst) =
+            *reinterpret_cast<const uint4*>(p.v_new + src);
       }
-      wait_vector_memory();
     }
+    if (wrote) wait_vector_memory();
   }
   if (b != (int)blockIdx.z || s0 != hs0 || s1 != hs1)
     ids = load_ids(s0, s1, my_n, 0);               // the speculation did not apply
@@ -883,6 +891,42 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) any_bad |= sm_flag[w];
   const size_t prow = ((size_t)b * p.num_kv_heads + kvh) * p.max_splits;   // partial rows
+  if constexpr (M * D >= 4 * NT) {
+    // Four or more elements per thread: four consecutive dims at a time, and
+    // the partial goes out as 16-byte stores with the same coherent policy.
+    const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+        p.ws_o + (prow + split) * M * D, 0, M * D * 4, kBufferRsrcWord3);
+    for (int i4 = tid; i4 < R * D / 4; i4 += NT) {
+      const int g = (i4 * 4) / D;                  // row
+      const int d = (i4 * 4) % D;
+      float mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, sm_m[w][g]);
+      float L = 0.f;
+      f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float mw = sm_m[w][g];
+        const float a = mw > kNegInf ? fast_exp2(mw - mx) : 0.f;
+        L = fmaf(a, sm_l[w][g], L);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sm_acc(w, g, d));
+        O.x = fmaf(a, v.x, O.x); O.y = fmaf(a, v.y, O.y);
+        O.z = fmaf(a, v.z, O.z); O.w = fmaf(a, v.w, O.w);
+      }
+      const f32x4 o = O / L;
+      const float lse2 = any_bad ? __builtin_nanf("") : mx + log2f(L);
+      if (nsplit == 1) {
+        const float nan = __builtin_nanf("");
+        *reinterpret_cast<f32x4*>(p.out + row_index(g) * D + d) =
+            any_bad ? f32x4{nan, nan, nan, nan} : o;
+        if (p.out_lse && d == 0) p.out_lse[row_index(g)] = lse2 * kLn2;
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), dst,
+                                               (g * D + d) * 4, 0, kCachePolicySc1);
+        if (d == 0) store_coherent(&p.ws_lse[(prow + split) * M + g], lse2);
+      }
+    }
+  } else {
   for (int idx = tid; idx < R * D; idx += NT) {
     const int g = idx / D;                         // row
     const int d = idx % D;
@@ -906,6 +950,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       store_coherent(&p.ws_o[((prow + split) * M + g) * D + d], o);
       if (d == 0) store_coherent(&p.ws_lse[(prow + split) * M + g], lse2);
     }
+  }
   }
   if (nsplit == 1) return;
 
@@ -952,8 +997,18 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   float* sm_w = sm_buf;                            // [M][64]
   float* sm_lse = sm_buf + M * kWave;              // [M] merged base-2 lse
   float4* sm_red = reinterpret_cast<float4*>(sm_buf + M * kWave + 4 * ((M + 3) / 4));
-  for (int g = wave; g < M; g += WAVES) {
-    const float x = lane < nsplit ? load_coherent(&p.ws_lse[(prow + lane) * M + g]) : kNegInf;
+  constexpr int RPW = (M + WAVES - 1) / WAVES;    // rows per wave
+  float xs[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {                  // all of this wave's lse loads at once
+    const int g = wave + r * WAVES;
+    xs[r] = (g < M && lane < nsplit) ? load_coherent(&p.ws_lse[(prow + lane) * M + g]) : kNegInf;
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int g = wave + r * WAVES;
+    if (g >= M) break;
+    const float x = xs[r];
     const bool nan = __any(x != x);
     const float mx = class_max<1>(x);
     const float w = lane < nsplit ? fast_exp2(x - mx) : 0.f;

@@ -274,7 +274,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
                               const int32_t* block_tables, const int32_t* context_lens,
                               int32_t max_context_len, float softmax_scale, float* out,
                               float* out_lse, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool append_tail = false) {
   gqa_status st = check_shape(s);
   if (st != GQA_OK) return st;
   if (max_context_len < 0)
@@ -289,7 +289,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
     return fail(GQA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
   if (!fp8 && (k_scale || v_scale))
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
-  if (positions && fp8)
+  if ((positions || append_tail) && fp8)
     return fail(GQA_ERR_UNSUPPORTED, "the fused append supports bf16 pools only");
   const int G = s->num_q_heads / s->num_kv_heads;
   if (num_queries < 1) return fail(GQA_ERR_INVALID_ARG, "num_queries %d < 1", num_queries);
@@ -300,7 +300,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   if (s->num_seqs == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(GQA_ERR_INVALID_ARG, "decode: NULL device pointer");
-  if (positions && (!k_new || !v_new))
+  if ((positions || append_tail) && (!k_new || !v_new))
     return fail(GQA_ERR_INVALID_ARG, "append: NULL k_new/v_new");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
@@ -337,6 +337,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
   p.positions = positions;
+  p.append_tail = append_tail ? 1 : 0;
   p.out = out;
   p.out_lse = out_lse;
   p.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
@@ -384,6 +385,16 @@ gqa_status gqa_paged_decode_multi_query(const gqa_paged_shape* s, int32_t num_qu
                      k_scale, v_scale, nullptr, nullptr, nullptr, block_tables, context_lens,
                      max_context_len, softmax_scale, out, out_lse, workspace, workspace_bytes,
                      stream);
+}
+
+gqa_status gqa_paged_decode_multi_query_append(
+    const gqa_paged_shape* s, int32_t num_queries, const void* q, const void* k_new,
+    const void* v_new, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t max_context_len, float softmax_scale, float* out,
+    float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(s, num_queries, q, k_cache, v_cache, nullptr, nullptr, k_new, v_new,
+                     nullptr, block_tables, context_lens, max_context_len, softmax_scale, out,
+                     out_lse, workspace, workspace_bytes, stream, true);
 }
 
 gqa_status gqa_paged_decode_append_attention(

@@ -237,6 +237,29 @@ gqa_status gqa_paged_decode_multi_query(const gqa_paged_shape* shape, int32_t nu
                                         hipStream_t stream);
 
 /*
+ * gqa_paged_decode_multi_query_append — the fused verification step: commit
+ * the Q new tokens of every sequence, then attend for all Q positions, in one
+ * kernel.
+ *   k_new, v_new  [B][Q][H_kv][d_h] bf16: row i goes to position
+ *                 context_lens[b] - Q + i (the sequence's last Q tokens)
+ *   other arguments as gqa_paged_decode_multi_query (k_cache/v_cache are
+ *   written at those Q slots only).  Same results as gqa_kv_append_tokens at
+ *   those positions followed by gqa_paged_decode_multi_query.  A sequence with
+ *   an invalid length (NaN outputs) appends nothing.  bf16 pools only.
+ */
+gqa_status gqa_paged_decode_multi_query_append(const gqa_paged_shape* shape,
+                                               int32_t num_queries, const void* q,
+                                               const void* k_new, const void* v_new,
+                                               void* k_cache, void* v_cache,
+                                               const int32_t* block_tables,
+                                               const int32_t* context_lens,
+                                               int32_t max_context_len,
+                                               float softmax_scale,
+                                               float* out, float* out_lse,
+                                               void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
+
+/*
  * gqa_paged_decode_append_attention — one fused decode step ("forward and
  * commit"): write each sequence's new token into the cache, then attend over
  * context_lens[b] tokens that include it, in a single kernel.

@@ -127,3 +127,27 @@ def test_speculative_verify_full_size(gpu):
     ref, ref_lse = _reference(case)
     out, lse = _verify_step(gpu, case, to_device(case))
     assert_parity(out, lse, ref, ref_lse, "verify 8K")
+
+
+@pytest.mark.parametrize("hq,hkv,nq,bs", [(32, 8, 4, 16), (64, 8, 2, 32), (8, 8, 16, 16),
+                                          (16, 8, 3, 16)])
+def test_fused_verify_step_matches_two_calls_bitwise(gpu, hq, hkv, nq, bs):
+    """Fused append + multi-position attention equals the append followed by the
+    attention call, bit for bit, and leaves the same cache."""
+    lens = [nq, 40, 1000, 3333]
+    spec = small_spec(num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                      block_size=bs, context=3333, case_id=6600 + hq + nq)
+    case = make_multi_query_case(spec, nq, seed=9, context_lens=lens)
+    ref, ref_lse = _reference(case)
+    d1, d2 = to_device(case), to_device(case)
+    o1, l1 = _verify_step(gpu, case, d1)
+    o2, l2 = gpu.paged_decode_multi_query_append(d2["q"], d2["k_new"], d2["v_new"], d2["k_cache"],
+                                                 d2["v_cache"], d2["block_tables"],
+                                                 d2["context_lens"], max(lens))
+    torch.cuda.synchronize()
+    o2, l2 = o2.cpu().numpy().astype(np.float64), l2.cpu().numpy().astype(np.float64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    bits = lambda t: t.view(torch.int16)                 # NaN-poisoned slots compare by bits
+    assert torch.equal(bits(d1["k_cache"]), bits(d2["k_cache"]))
+    assert torch.equal(bits(d1["v_cache"]), bits(d2["v_cache"]))
+    assert_parity(o2, l2, ref, ref_lse, "fused verify")
