@@ -22,6 +22,13 @@ For every sequence b and query head h (g = h // G, ctx = context_lens[b]):
   out[b, h] = sum_t w_t v_t ;  lse[b, h] = max s + ln sum exp(s - max s)
 An empty context (ctx = 0) gives out = 0 and lse = -inf (a reading: the pages
 do not treat it).
+
+Sliding window (``sliding_window = w > 0``): the query, at position ctx - 1,
+attends only to the w most recent tokens, ctx - w .. ctx - 1 (all of them when
+ctx <= w).  *Module 10*, "Parameter count alone does not determine cache size"
+(sliding-window attention keeps a bounded recent context; Mistral 7B uses a
+4,096-token window); *The Mathematics of Transformer Inference* §5 (local
+layers see only the most recent w tokens, so their cache is bounded by w).
 """
 import numpy as np
 
@@ -59,13 +66,15 @@ def dense_decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_
 
 
 def paged_decode_attention(q_bits, k_pool, v_pool, block_tables, context_lens, block_size,
-                           softmax_scale, kv_dtype="bf16", k_scale=None, v_scale=None):
+                           softmax_scale, kv_dtype="bf16", k_scale=None, v_scale=None,
+                           sliding_window=0):
     """Paged decode attention for a batch.
 
     q_bits      uint16 [B][H_q][d] (bf16 bit patterns)
     k_pool/v_pool uint16 (bf16) or uint8 (fp8 codes) [NB][H_kv][BS][d]
     block_tables int [B][max_blocks]; context_lens int [B]
     k_scale/v_scale float32 [NB][H_kv] for fp8 (dequantised value = decode(code) * scale)
+    sliding_window  w > 0 restricts each query to its w most recent tokens (0: all)
     Returns (out float64 [B][H_q][d], lse float64 [B][H_q]).
     """
     q = bf16_to_float64(q_bits)
@@ -86,5 +95,6 @@ def paged_decode_attention(q_bits, k_pool, v_pool, block_tables, context_lens, b
             vs = np.asarray(v_scale, dtype=np.float64)[phys, :].T
             kr = kr * ks[:, :, None]
             vr = vr * vs[:, :, None]
-        out[b], lse[b] = dense_decode_attention(q[b], kr, vr, softmax_scale)
+        lo = max(0, ctx - sliding_window) if sliding_window > 0 else 0
+        out[b], lse[b] = dense_decode_attention(q[b], kr[:, lo:], vr[:, lo:], softmax_scale)
     return out, lse

@@ -21,7 +21,8 @@ to the tokens 0 .. ctx - Q + i, i.e. to the first n_i = ctx - Q + 1 + i rows:
   n_i tokens.
 Readings (the pages do not treat them): ctx = 0 gives out = 0 and lse = -inf
 for every query; 0 < ctx < Q is malformed (a query would sit before position 0)
-and gives NaN.
+and gives NaN.  With a sliding window w > 0, query i also drops the tokens
+before position ctx - Q + i - w + 1 (see ``oracle.attention``).
 """
 import numpy as np
 
@@ -31,7 +32,8 @@ from .cache import gather_sequence
 
 
 def paged_multi_query_attention(q_bits, k_pool, v_pool, block_tables, context_lens, block_size,
-                                softmax_scale, kv_dtype="bf16", k_scale=None, v_scale=None):
+                                softmax_scale, kv_dtype="bf16", k_scale=None, v_scale=None,
+                                sliding_window=0):
     """q_bits uint16 [B][Q][H_q][d]; pools, tables, scales as ``paged_decode_attention``.
 
     Returns (out float64 [B][Q][H_q][d], lse float64 [B][Q][H_q]).
@@ -57,6 +59,7 @@ def paged_multi_query_attention(q_bits, k_pool, v_pool, block_tables, context_le
             vr = vr * np.asarray(v_scale, dtype=np.float64)[phys, :].T[:, :, None]
         for i in range(Q):
             n = ctx - Q + 1 + i                        # tokens up to and including position ctx-Q+i
-            out[b, i], lse[b, i] = dense_decode_attention(q[b, i], kr[:, :n], vr[:, :n],
+            lo = max(0, n - sliding_window) if sliding_window > 0 else 0
+            out[b, i], lse[b, i] = dense_decode_attention(q[b, i], kr[:, lo:n], vr[:, lo:n],
                                                           softmax_scale)
     return out, lse
