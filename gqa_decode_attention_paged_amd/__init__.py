@@ -40,7 +40,7 @@ class PagedShape(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("sliding_window", ctypes.c_int32)]
 
 
 class GqaError(RuntimeError):
@@ -131,10 +131,12 @@ def _kv_dtype(cache) -> int:
     raise TypeError(f"unsupported KV cache dtype {cache.dtype}")
 
 
-def make_shape(num_seqs, num_q_heads, k_cache, block_tables, batch_invariant=False) -> PagedShape:
+def make_shape(num_seqs, num_q_heads, k_cache, block_tables, batch_invariant=False,
+               sliding_window=0) -> PagedShape:
     nb, hkv, bs, d = k_cache.shape
     return PagedShape(num_seqs, num_q_heads, hkv, d, bs, nb, block_tables.shape[1],
-                      _kv_dtype(k_cache), GQA_FLAG_BATCH_INVARIANT if batch_invariant else 0)
+                      _kv_dtype(k_cache), GQA_FLAG_BATCH_INVARIANT if batch_invariant else 0,
+                      int(sliding_window))
 
 
 def num_splits(context_len: int) -> int:
@@ -173,13 +175,13 @@ def multi_query_workspace_size(shape: PagedShape, num_queries: int, max_context_
 def paged_decode_multi_query(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                              softmax_scale=None, k_scale=None, v_scale=None, out=None,
                              out_lse=None, workspace=None, return_lse=True,
-                             batch_invariant=False):
+                             batch_invariant=False, sliding_window=0):
     """Attention for Q consecutive query positions per sequence, q [B][Q][H_q][d_h]: query i
     sits at position context_lens[b] - Q + i and attends causally.  Returns (out, lse)."""
     import torch
     lib = load()
     B, Q, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -199,12 +201,12 @@ def paged_decode_multi_query(q, k_cache, v_cache, block_tables, context_lens, ma
 
 def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                            softmax_scale=None, k_scale=None, v_scale=None, out=None,
-                           out_lse=None, workspace=None, return_lse=True, batch_invariant=False):
+                           out_lse=None, workspace=None, return_lse=True, batch_invariant=False, sliding_window=0):
     """Decode attention for a batch; returns (out, lse) (lse None if not requested)."""
     import torch
     lib = load()
     B, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -224,13 +226,13 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
 def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tables,
                                     context_lens, max_context_len, softmax_scale=None, out=None,
                                     out_lse=None, workspace=None, return_lse=True,
-                                    batch_invariant=False):
+                                    batch_invariant=False, sliding_window=0):
     """Fused verification step: commit k_new/v_new [B][Q][H_kv][d_h] at positions
     context_lens[b] - Q + i, then attend for the Q positions (one kernel)."""
     import torch
     lib = load()
     B, Q, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -258,12 +260,12 @@ def make_workspace(shape: PagedShape, max_context_len: int, device):
 def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, block_tables,
                                   context_lens, max_context_len, softmax_scale=None, out=None,
                                   out_lse=None, workspace=None, return_lse=True,
-                                  batch_invariant=False):
+                                  batch_invariant=False, sliding_window=0):
     """Fused decode step: commit the new token at positions[b], then attend (one kernel)."""
     import torch
     lib = load()
     B, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:

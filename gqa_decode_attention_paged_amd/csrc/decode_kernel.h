@@ -82,6 +82,7 @@ struct DecodeParams {
   int32_t group_shift;          // log2(G)
   int32_t num_queries;          // Q query positions per sequence (the last Q tokens)
   int32_t rows;                 // R = G * Q rows per (sequence, KV head)
+  int32_t window;               // sliding window w (0: attend to the whole context)
   int32_t num_blocks;
   int32_t max_blocks;
   int32_t max_splits;           // row stride of the split partials
@@ -338,8 +339,17 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     const int nch = (s1_ - s0_ + CT - 1) / CT;
     return wave < nch ? (nch - wave + WAVES - 1) / WAVES : 0;
   };
-  const SplitPlan hplan = split_plan(p.hint_ctx, p.target_splits);
-  const int hs0 = (int)blockIdx.x * hplan.split_tokens;
+  // With a sliding window, a sequence's splits cover only its attended span,
+  // from the start of the block holding the first token any of its queries
+  // sees: blocks wholly before the window are never read.
+  auto span_base = [&](int c) {
+    if (p.window <= 0) return 0;
+    const int first = c - p.num_queries + 1 - p.window;      // query 0's first token
+    return first > 0 ? first / BS * BS : 0;
+  };
+  const int hbase = span_base(p.hint_ctx);
+  const SplitPlan hplan = split_plan(p.hint_ctx - hbase, p.target_splits);
+  const int hs0 = hbase + (int)blockIdx.x * hplan.split_tokens;
   const int hs1 = min(p.hint_ctx, hs0 + hplan.split_tokens);
   const int hmy_n = (int)blockIdx.x < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
   int ids = load_ids(hs0, hs1, hmy_n, 0);
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     const int pi = (p.positions && lane < nseq) ? p.positions[lane] : -1;
     const int c0 = __builtin_amdgcn_readfirstlane(ci);
     if (__ballot(lane < nseq && ci != c0) != 0) {    // lengths differ: share out
-      const int cw = (ci > 0 && ci <= p.hint_ctx && ci <= p.max_blocks * BS) ? ci : 0;
+      const int cw = (ci > 0 && ci <= p.hint_ctx && ci <= p.max_blocks * BS) ? ci - span_base(ci) : 0;
       const double tot = wave_sum_f64((double)cw);
       const double f = tot > 0.0 ? (double)cw / tot : 0.0;
       const int slots = S * nseq;
@@ -392,7 +402,9 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // A sequence holds its Q query positions as its last Q tokens, so 0 < ctx < Q
   // is invalid (ctx = 0 stays the empty sequence).
   const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS || (ctx > 0 && ctx < Q);
-  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx, p.proportional ? slots_b : p.target_splits);
+  const int base = ctx_bad ? 0 : span_base(ctx);    // first token of the attended span
+  const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx - base,
+                                    p.proportional ? slots_b : p.target_splits);
   // Row m of this (sequence, KV head) is query i = m / G of head h0 + m % G; its
   // flat index into q [B][Q][H_q][D], out and out_lse.  Query i sits at position
   // ctx - Q + i and attends to the tokens before it and itself.
@@ -400,10 +412,14 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     return ((size_t)b * Q + (m >> p.group_shift)) * p.num_q_heads + h0 + (m & (G - 1));
   };
   auto row_limit = [&](int m) { return ctx - Q + 1 + (m >> p.group_shift); };   // tokens < this
-  const bool too_long = ctx > p.hint_ctx || plan.num_splits > slots_b;
+  auto row_low = [&](int m) {                      // and tokens >= this (sliding window)
+    return p.window > 0 ? max(0, row_limit(m) - p.window) : 0;
+  };
+  const bool too_long = ctx > p.hint_ctx || plan.num_splits > slots_b ||
+                        plan.num_splits > p.max_splits;
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
-  const int owner = (!degenerate && pos >= 0 && pos < ctx) ? pos / plan.split_tokens : 0;
-  const bool pos_in_split = !degenerate && pos >= 0 && pos < ctx;
+  const bool pos_in_split = !degenerate && pos >= base && pos < ctx;
+  const int owner = pos_in_split ? (pos - base) / plan.split_tokens : 0;
   if (p.positions && split == owner && !pos_in_split) append_rows(p, b, kvh, pos, D, BS);
 
   if (degenerate) {
@@ -416,7 +432,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   }
   const int nsplit = plan.num_splits;
   if (split >= nsplit) return;
-  const int s0 = split * plan.split_tokens;
+  const int s0 = base + split * plan.split_tokens;
   const int s1 = min(ctx, s0 + plan.split_tokens);
   const int my_n = wave_chunks(s0, s1);
   // Fused append: the token at `pos`, or with append_tail the Q query positions
@@ -526,6 +542,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       qop[kb] = as_bf16x8(v);
     }
     const int hd_limit = hd < R ? row_limit(hd) : 0;   // this lane's row sees tokens < this
+    const int hd_low = hd < R ? row_low(hd) : 0;       // and >= this
     f32x4 acc[NN];                        // rows: heads 4*qd + r; columns: dims 16*n + hd
 #pragma unroll
     for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -558,6 +575,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       const int t0 = chunk_start(j);
       const int nvalid = s1 - t0;
       const int lim = min(nvalid, hd_limit - t0);        // tokens t < lim count for row hd
+      const int lo = hd_low - t0;                        // and t >= lo
       f32x4 sc[2];
 #pragma unroll
       for (int t16 = 0; t16 < 2; ++t16) {
@@ -581,7 +599,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * t16 + 4 * qd + r;
           float x = sc[t16][r] * p.scale_log2;
-          if (t >= lim) x = kNegInf;           // split tail, causal limit, unused rows
+          if (t >= lim || t < lo) x = kNegInf;  // split tail, causal limit, window, unused rows
           s[t16 * 4 + r] = x;
           cmax = fmaxf(cmax, x);
         }
@@ -706,6 +724,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     // of this lane's 8 dims.
     const int sg = lane % M;
     const int sg_limit = sg < R ? row_limit(sg) : 0;     // row sg sees tokens < this
+    const int sg_low = sg < R ? row_low(sg) : 0;         // and >= this
     float acc[M][8];
 #pragma unroll
     for (int g = 0; g < M; ++g)
@@ -723,6 +742,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       const int t0 = chunk_start(j);
       const int nvalid = s1 - t0;                      // rows t < nvalid are real
       const int lim = min(nvalid, sg_limit - t0);      // tokens t < lim count for row sg
+      const int lo = sg_low - t0;                      // and t >= lo
       if constexpr (SLOW) {
         // zero V rows past the split end (their slots may hold NaN poison)
 #pragma unroll
@@ -779,7 +799,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
             a += (v.x + v.y) + (v.z + v.w);
           }
           tot = a * p.scale_log2;
-          if (t >= lim) tot = kNegInf;         // split tail, causal limit, unused rows
+          if (t >= lim || t < lo) tot = kNegInf;  // tail, causal limit, window, unused rows
         }
         sc[q] = tot;
         cmax = fmaxf(cmax, tot);

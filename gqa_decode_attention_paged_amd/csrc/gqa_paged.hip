@@ -65,6 +65,8 @@ gqa_status check_shape(const gqa_paged_shape* s) {
     return fail(GQA_ERR_UNSUPPORTED, "kv_dtype=%d unknown", s->kv_dtype);
   if (s->flags & ~GQA_FLAG_BATCH_INVARIANT)
     return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)s->flags);
+  if (s->sliding_window < 0)
+    return fail(GQA_ERR_INVALID_ARG, "sliding_window %d < 0", s->sliding_window);
   if ((int64_t)s->max_blocks_per_seq * s->block_size > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size overflows int32");
   return GQA_OK;
@@ -98,9 +100,25 @@ WorkspaceLayout workspace_layout(const gqa_paged_shape* s, int max_splits, int n
   return w;
 }
 
-int max_splits_for(int32_t max_context_len) {
-  const int ms = gqa::split_plan(max_context_len).num_splits;
-  return ms < 1 ? 1 : ms;
+// Splits a launch or a workspace must provide for every attended length up to
+// `len` under target `target`: a split plan never uses more than
+// min(target, ceil(len / kMinSplitTokens)), while the plan of `len` itself may
+// round to fewer than a shorter length's plan.
+int split_bound(int64_t len, int target) {
+  const int64_t n = (len + gqa::kMinSplitTokens - 1) / gqa::kMinSplitTokens;
+  const int64_t b = n < target ? n : target;
+  return b < 1 ? 1 : (int)b;
+}
+
+int max_splits_for(int32_t max_context_len) { return split_bound(max_context_len, gqa::kMaxSplits); }
+
+// Longest attended span any sequence can have: the whole hint, or with a
+// sliding window the window plus the other query positions plus the partial
+// block the span starts in.
+int64_t max_span(const gqa_paged_shape* s, int32_t max_context_len, int32_t num_queries) {
+  if (s->sliding_window <= 0) return max_context_len;
+  const int64_t w = (int64_t)s->sliding_window + num_queries - 1 + s->block_size - 1;
+  return w < max_context_len ? w : max_context_len;
 }
 
 // Kernel dispatch over the supported (D, BS, rows M, dtype, waves) combinations.
@@ -211,13 +229,16 @@ int32_t gqa_decode_num_splits(int32_t context_len) {
 
 size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max_context_len) {
   if (check_shape(shape) != GQA_OK || max_context_len < 0) return 0;
-  return workspace_layout(shape, max_splits_for(max_context_len), 1).total;
+  return workspace_layout(shape, split_bound(max_span(shape, max_context_len, 1), gqa::kMaxSplits),
+                          1).total;
 }
 
 size_t gqa_paged_multi_query_workspace_size(const gqa_paged_shape* shape, int32_t num_queries,
                                             int32_t max_context_len) {
   if (check_shape(shape) != GQA_OK || max_context_len < 0 || num_queries < 1) return 0;
-  return workspace_layout(shape, max_splits_for(max_context_len), num_queries).total;
+  return workspace_layout(shape,
+                          split_bound(max_span(shape, max_context_len, num_queries), gqa::kMaxSplits),
+                          num_queries).total;
 }
 
 static gqa_status append_impl(const gqa_paged_shape* s, int32_t num_tokens, const void* k_new,
@@ -305,7 +326,8 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
     return fail(GQA_ERR_INVALID_ARG, "decode: q, caches, new rows and out must be 16-byte aligned");
-  const WorkspaceLayout wl = workspace_layout(s, max_splits_for(max_context_len), num_queries);
+  const int ws_splits = split_bound(max_span(s, max_context_len, num_queries), gqa::kMaxSplits);
+  const WorkspaceLayout wl = workspace_layout(s, ws_splits, num_queries);
   if (!workspace || workspace_bytes < wl.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 wl.total);
@@ -315,8 +337,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows), fp8, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
   const int target = target_splits(s, fn, waves * 64);
-  int launch_splits = gqa::split_plan(max_context_len, target).num_splits;
-  if (launch_splits < 1) launch_splits = 1;
+  const int launch_splits = split_bound(max_span(s, max_context_len, num_queries), target);
   if ((int64_t)launch_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   // Ragged batches: share each KV head's slots out by sequence length (one
@@ -351,7 +372,8 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.rows = rows;
   p.num_blocks = s->num_blocks;
   p.max_blocks = s->max_blocks_per_seq;
-  p.max_splits = max_splits_for(max_context_len);
+  p.max_splits = ws_splits;
+  p.window = s->sliding_window;
   p.hint_ctx = max_context_len;
   p.target_splits = target;
   p.proportional = proportional ? 1 : 0;

@@ -25,6 +25,11 @@
  *  - FP8 KV: E4M3 in the finite-only convention (max 448), dequantised inside the
  *    kernel with a scale.  *Module 10*, number-format table; *The Mathematics of
  *    Transformer Inference* §11.
+ *  - Sliding window: a local-attention layer keeps only a bounded recent context
+ *    (the w most recent tokens; Mistral 7B uses w = 4096).  *Module 10*,
+ *    "Parameter count alone does not determine cache size"; *The Mathematics of
+ *    Transformer Inference* §5.  With a window, table entries of blocks that lie
+ *    wholly before every query's window are never read (they may be released).
  *  - Several query positions per sequence: speculative decoding verifies k
  *    drafted tokens with one target pass over the committed prefix plus those
  *    positions, each attending causally.  *LLM Inference Systems Engineering*
@@ -101,6 +106,8 @@ typedef struct gqa_paged_shape {
   int32_t max_blocks_per_seq;  /* row length of block_tables                          */
   int32_t kv_dtype;            /* gqa_kv_dtype                                        */
   int32_t flags;               /* GQA_FLAG_* bits (0 = default)                      */
+  int32_t sliding_window;      /* w > 0: each query attends to its w most recent     */
+                               /* tokens, itself included; 0: the whole context      */
 } gqa_paged_shape;
 
 /*
@@ -141,8 +148,8 @@ gqa_status gqa_kv_append_tokens(const gqa_paged_shape* shape, int32_t num_tokens
 /*
  * gqa_decode_num_splits — the batch-invariant context split plan (host
  * function, no GPU): how many partial attentions a sequence of `context_len`
- * tokens is cut into under GQA_FLAG_BATCH_INVARIANT, which is also the most
- * any plan uses.  0 for context_len <= 0.
+ * attended tokens is cut into under GQA_FLAG_BATCH_INVARIANT.  0 for
+ * context_len <= 0.  No plan uses more than min(64, ceil(context_len / 128)).
  */
 int32_t gqa_decode_num_splits(int32_t context_len);
 

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 def _shape(**kw):
     from gqa_decode_attention_paged_amd import PagedShape
     base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
-                num_blocks=1024, max_blocks_per_seq=600, kv_dtype=0, flags=0)
+                num_blocks=1024, max_blocks_per_seq=3000, kv_dtype=0, flags=0, sliding_window=0)
     base.update(kw)
     return PagedShape(**base)
 
@@ -71,6 +71,31 @@ def test_workspace_size_formula(lib):
     assert gqa.workspace_size(s, 8192) == lse_off + rows * 4
     assert gqa.workspace_size(_shape(head_dim=96), 8192) == 0      # unsupported
     assert gqa.workspace_size(s, -1) == 0
+
+
+def test_workspace_covers_every_plan_up_to_the_hint(lib):
+    """The plan of a 10000-token hint rounds to 63 splits while an 8192-token sequence
+    under it needs 64: the workspace provides min(64, ceil(len / 128)) splits."""
+    import gqa_decode_attention_paged_amd as gqa
+    assert gqa.num_splits(10000) == 63 and gqa.num_splits(8192) == 64
+    s = _shape()
+    rows = 2 * 32 * 64
+    o_off = (2 * 8 * 64 * 4 + 255) // 256 * 256
+    lse_off = (o_off + rows * 128 * 4 + 255) // 256 * 256
+    assert gqa.workspace_size(s, 10000) == lse_off + rows * 4
+
+
+def test_sliding_window_bounds_the_workspace(lib):
+    """With a window the split partials cover the window's span, not the hint."""
+    import gqa_decode_attention_paged_amd as gqa
+    full = gqa.workspace_size(_shape(), 32768)
+    win = gqa.workspace_size(_shape(sliding_window=1000), 32768)
+    span = 1000 + 16 - 1                           # window + partial first block
+    rows = 2 * 32 * -(-span // 128)
+    o_off = (2 * 8 * 64 * 4 + 255) // 256 * 256
+    lse_off = (o_off + rows * 128 * 4 + 255) // 256 * 256
+    assert win == lse_off + rows * 4 and win < full
+    assert _call_decode(lib, _shape(sliding_window=-1)) == 1
 
 
 def _call_decode(lib, shape, ws_bytes=1 << 30, ptr=16, **over):
