@@ -8,8 +8,9 @@ checked by eye against the pages it cites:
 
 * ``attention.paged_decode_attention`` — the definition of single-token decode
   attention over a paged KV cache, written out in float64.
-* ``cache.kv_append`` / ``cache.kv_append_tokens`` / ``cache.gather_sequence`` —
-  the block-table scatter and gather, as integer indexing.
+* ``cache.kv_append`` / ``cache.kv_append_tokens`` / ``cache.gather_sequence`` /
+  ``cache.copy_blocks`` — the block-table scatter, gather and copy-on-write
+  block copy, as integer indexing.
 * ``multi_query.paged_multi_query_attention`` — several consecutive query
   positions per sequence (speculative verification), each attending causally.
 * ``fp8.decode_e4m3fn`` — OCP FP8 E4M3 (finite-only, max 448) decoding from the
@@ -24,7 +25,7 @@ itself (brute force, a float64 library routine, closed forms, invariants and
 values printed on the pages).  No function here is "parity unpinned".
 """
 from .attention import paged_decode_attention, dense_decode_attention
-from .cache import kv_append, kv_append_tokens, gather_sequence
+from .cache import kv_append, kv_append_tokens, gather_sequence, copy_blocks
 from .multi_query import paged_multi_query_attention
 from .fp8 import decode_e4m3fn
 from .bf16 import bf16_to_float64
@@ -33,7 +34,7 @@ from .formulas import kv_cache_bytes, decode_attention_flops, decode_attention_i
 
 __all__ = [
     "paged_decode_attention", "dense_decode_attention", "kv_append", "kv_append_tokens",
-    "gather_sequence", "paged_multi_query_attention",
+    "gather_sequence", "copy_blocks", "paged_multi_query_attention",
     "decode_e4m3fn", "bf16_to_float64", "chunked_attention", "merge_partials",
     "kv_cache_bytes", "decode_attention_flops", "decode_attention_intensity",
 ]

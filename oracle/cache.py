@@ -13,7 +13,13 @@ Cites:
   holds positions already forwarded; each step first commits the pending
   token's K/V, then attends.
 * *The Mathematics of Transformer Inference* (hs-black), §1: decode reads the
-  cache for attention and appends the new token's own K and V.
+  cache for attention and appends the new token's own K and V; §9: sequences
+  may share physical blocks, with reference counts and copy-on-write.
+* Copy-on-write: *Module 10*, "Share only state with the same identity" (a
+  sequence about to write into a shared, not yet full block first gets a
+  private copy, so the other sequence's state is unchanged; full prefix blocks
+  stay shared); *Stochastic Parrot* §6.4 (branches point at the same read-only
+  block and get a new one on a divergent write).
 
 Pool layout (a reading; the pages fix no layout): ``pool[num_blocks][H_kv][BS][d_h]``;
 token t of sequence b lives in physical block ``block_table[b][t // BS]`` at
@@ -76,3 +82,27 @@ def kv_append_tokens(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
             k_out[blk, :, pos % block_size, :] = k_new[b, j]
             v_out[blk, :, pos % block_size, :] = v_new[b, j]
     return k_out, v_out
+
+
+def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, src_blocks, dst_blocks,
+                k_scale=None, v_scale=None):
+    """Copy whole physical blocks (every KV head, every slot, K and V, and the
+    fp8 scales when given): block ``dst_blocks[j]`` becomes a copy of
+    ``src_blocks[j]``, as taken before the call.  A pair with an id outside the
+    pool is skipped.  Returns new pools (and scales); inputs are not modified."""
+    nb = k_pool.shape[0]
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    ks_out = None if k_scale is None else np.array(k_scale, copy=True)
+    vs_out = None if v_scale is None else np.array(v_scale, copy=True)
+    for src, dst in zip(np.asarray(src_blocks), np.asarray(dst_blocks)):
+        src, dst = int(src), int(dst)
+        if not (0 <= src < nb and 0 <= dst < nb):
+            continue
+        k_out[dst] = k_pool[src]
+        v_out[dst] = v_pool[src]
+        if ks_out is not None:
+            ks_out[dst] = k_scale[src]
+            vs_out[dst] = v_scale[src]
+    if ks_out is None:
+        return k_out, v_out
+    return k_out, v_out, ks_out, vs_out
