@@ -16,6 +16,12 @@ Workload ``verify4`` is the verification pass of speculative decoding on the
 8K grouped-query shape: each step commits 4 new tokens (the pending one and 3
 drafts) and attends for all 4 positions, in one fused kernel.
 
+Workload ``cow_fork`` measures the copy-on-write block copy instead: 256 prompts
+on the 8K grouped-query pool geometry each fork into 8 parallel samples, so each
+prompt's partially filled last block is copied to 7 fresh blocks (1792 copies,
+one kernel launch per step); its bytes are the unique source blocks read plus
+the destination blocks written.
+
 Prints one JSON line (rank 0, N=1).  `value` = algorithmic KV bytes per step /
 step time.  `roofline.achieved` = the same bytes / the decode-attention call's
 average duration measured with HIP events on the launch stream.  The float64
@@ -48,6 +54,33 @@ def kv_bytes_per_step(spec, context_lens):
         nb = (ctx + spec.block_size - 1) // spec.block_size
         total += int(nb.sum()) * spec.num_kv_heads * 2 * 4
     return total
+
+
+FORK_PROMPTS, FORK_SAMPLES = 256, 8     # cow_fork: prompts x parallel samples each
+
+
+def fork_geometry():
+    """(pairs, H_kv, d_h, block_size, blocks per rotation range, algorithmic bytes) of
+    the cow_fork step: every prompt's source block is read once and each of its
+    FORK_SAMPLES - 1 copies written once, K and V."""
+    from workloads import SPECS
+    s = SPECS["llama8b"]
+    pairs = FORK_PROMPTS * (FORK_SAMPLES - 1)
+    block_bytes = s.num_kv_heads * s.block_size * s.head_dim * 2 * 2      # K and V, bf16
+    return (pairs, s.num_kv_heads, s.head_dim, s.block_size, FORK_PROMPTS + pairs,
+            (FORK_PROMPTS + pairs) * block_bytes)
+
+
+def fork_pairs(np, seed, first_block):
+    """Seeded source/destination lists of one cow_fork range starting at first_block:
+    a random permutation of the range gives each prompt its source block and fresh
+    destination blocks; copies of one source are adjacent in the list."""
+    pairs, _, _, _, nblk, _ = fork_geometry()
+    perm = np.random.default_rng([seed, first_block]).permutation(nblk).astype(np.int32)
+    perm += first_block
+    src = np.repeat(perm[:FORK_PROMPTS], FORK_SAMPLES - 1)
+    dst = perm[FORK_PROMPTS:]
+    return src, dst
 
 
 def kernel_source_hash():
@@ -98,7 +131,8 @@ def write_traffic(workload, pmc_dir, kv_bytes):
     profiles/traffic_<workload>.json.  Counters are KiB per dispatch; each is scaled
     by (known copy bytes) / (what the same counter reads for the copy kernel)."""
     import statistics
-    is_decode = lambda n: "paged_decode_kernel" in n
+    kname = "kv_copy_blocks_kernel" if workload == "cow_fork" else "paged_decode_kernel"
+    is_decode = lambda n: kname in n
     is_copy = lambda n: "elementwise" in n and "Fill" not in n
     out = {"workload": workload, "kernel_source_sha": kernel_source_hash(),
            "algorithmic_bytes_per_call": kv_bytes}
@@ -155,7 +189,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b",
-                    choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4"])
+                    choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4",
+                             "cow_fork"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -176,6 +211,9 @@ def main():
     import numpy as np
 
     verify = args.workload == "verify4"          # 4 query positions on the 8K shape
+    if args.traffic_from and args.workload == "cow_fork":
+        write_traffic(args.workload, args.traffic_from, fork_geometry()[5])
+        return
     if args.traffic_from:
         from workloads import make_case, SPECS
         spec = SPECS["llama8b" if verify else args.workload]
@@ -200,6 +238,9 @@ def main():
         return
 
     gqa.load()
+    if args.workload == "cow_fork":
+        print(json.dumps(bench_block_copy(args, np, torch, gqa)), flush=True)
+        return
     dev = torch.device("cuda:0")
     spec = SPECS["llama8b" if verify else args.workload]
     case = (make_multi_query_case(spec, 4, seed=args.seed) if verify
@@ -245,41 +286,7 @@ def main():
             gqa.paged_decode_attention(q, kc, vc, bt, ctx, max_ctx, scale, ks, vs, out=out,
                                        out_lse=lse, workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    graph = None
-    if not args.no_graph:
-        # The K timed steps are recorded once into a HIP graph and replayed, so the
-        # GPU runs them back to back without Python launch gaps.  Every step still
-        # launches the full decode kernel on its own pool copy.
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            for i in range(args.steps):
-                step(args.warmup + i)
-        torch.cuda.synchronize()
-        graph.replay()                      # untimed: first replay uploads the graph
-        torch.cuda.synchronize()
-
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(args.warmup + i)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop)
-    ms_per_step = wall * 1e3 / args.steps
-    call_ms = gpu_ms / args.steps
+    ms_per_step, call_ms, graphed = _timed(torch, args, step)
     achieved = kv_bytes / (call_ms * 1e-3) / 1e9
     if verify:
         kernel = ("paged_decode_kernel (fused 4-token KV append + 4 query positions, split "
@@ -321,13 +328,114 @@ def main():
             "kernel": kernel,
             "kernel_us_events": round(call_ms * 1e3, 3),
             "timing": ("HIP events on the launch stream around one replay of a graph of the "
-                       "K steps (one kernel per step), divided by K" if graph is not None else
+                       "K steps (one kernel per step), divided by K" if graphed else
                        "HIP events around K eager steps, divided by K"),
         },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, kv_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _timed(torch, args, step):
+    """Warm up, record the K timed steps into a HIP graph (unless --no-graph), and
+    return (wall ms per step, event ms per step on the launch stream, graph used)."""
+    dev = torch.device("cuda:0")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / args.steps, start.elapsed_time(stop) / args.steps, graph is not None
+
+
+def bench_block_copy(args, np, torch, gqa):
+    """The cow_fork workload: one copy-on-write block-copy launch per step."""
+    dev = torch.device("cuda:0")
+    pairs, hkv, d, bs, nblk, alg_bytes = fork_geometry()
+    copies = min(64, math.ceil(ROTATE_BYTES / alg_bytes) + 1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    k = torch.randn((copies * nblk, hkv, bs, d), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((copies * nblk, hkv, bs, d), generator=gen, device=dev).to(torch.bfloat16)
+    lists = []
+    for c in range(copies):
+        src, dst = fork_pairs(np, args.seed, c * nblk)
+        lists.append((torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)))
+
+    def step(i):
+        src, dst = lists[i % copies]
+        gqa.kv_copy_blocks(k, v, src, dst)
+
+    ms_per_step, call_ms, graphed = _timed(torch, args, step)
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": "copy-on-write block copy HBM GB/s (unique source blocks read + copies "
+                  "written, % of MI355X peak) and µs/step",
+        "value": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "us_per_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) pools, random block placement; no weights)",
+        "config": {
+            "workload": "cow_fork", "prompts": FORK_PROMPTS, "samples_per_prompt": FORK_SAMPLES,
+            "copies_per_step": pairs, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
+            "kv_dtype": "bf16", "bytes_per_step": alg_bytes, "pool_ranges_rotated": copies,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": counted_traffic("cow_fork"),
+            "kernel": "kv_copy_blocks_kernel (copy-on-write block copy)",
+            "kernel_us_events": round(call_ms * 1e3, 3),
+            "timing": ("HIP events on the launch stream around one replay of a graph of the "
+                       "K steps (one kernel per step), divided by K" if graphed else
+                       "HIP events around K eager steps, divided by K"),
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        kh = np.random.default_rng(args.seed).integers(0, 1 << 16, (nblk, hkv, bs, d),
+                                                       dtype=np.uint16)
+        vh = kh[::-1].copy()
+        src, dst = fork_pairs(np, args.seed, 0)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.copy_blocks(kh, vh, src, dst)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        per = el / n
+        result["cpu_baseline"] = {
+            "value": round(alg_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} whole step(s) of cow_fork (one {nblk}-block range), numpy oracle "
+                      f"copy, 1 thread, {el:.1f} s total ({per * 1e3:.1f} ms/step)"}
+    return result
 
 
 if __name__ == "__main__":

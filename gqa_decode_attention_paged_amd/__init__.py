@@ -90,6 +90,8 @@ def load():
     lib.gqa_paged_decode_append_attention.restype = ctypes.c_int
     lib.gqa_paged_decode_workspace_init.argtypes = [S, ctypes.c_int32, _P, ctypes.c_size_t, _P]
     lib.gqa_paged_decode_workspace_init.restype = ctypes.c_int
+    lib.gqa_kv_copy_blocks.argtypes = [S, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
+    lib.gqa_kv_copy_blocks.restype = ctypes.c_int
     lib.gqa_kv_gather.argtypes = [S, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.gqa_kv_gather.restype = ctypes.c_int
     lib.gqa_last_error.argtypes = []
@@ -289,13 +291,24 @@ def workspace_init(shape: PagedShape, max_context_len: int, workspace):
         workspace.numel() * workspace.element_size(), _stream(workspace)))
 
 
+def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_scale=None):
+    """Copy-on-write block copy: block dst_blocks[j] of both pools (and the fp8 scales)
+    becomes a copy of src_blocks[j], in place."""
+    nb, hkv, bs, d = k_cache.shape
+    shape = PagedShape(1, hkv, hkv, d, bs, nb, 1, _kv_dtype(k_cache), 0, 0)
+    _check(load().gqa_kv_copy_blocks(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_scale), _ptr(v_scale), _ptr(src_blocks),
+                                     _ptr(dst_blocks), int(src_blocks.numel()),
+                                     _stream(k_cache)))
+
+
 def kv_gather(cache, block_tables, seq, num_tokens):
     """Copy sequence ``seq``'s first ``num_tokens`` rows out of a pool: [H_kv][T][d_h]."""
     import torch
     lib = load()
     nb, hkv, bs, d = cache.shape
     shape = PagedShape(block_tables.shape[0], hkv, hkv, d, bs, nb, block_tables.shape[1],
-                       _kv_dtype(cache), 0)
+                       _kv_dtype(cache), 0, 0)
     out = torch.empty((hkv, num_tokens, d), dtype=cache.dtype, device=cache.device)
     _check(lib.gqa_kv_gather(ctypes.byref(shape), _ptr(cache), _ptr(block_tables), int(seq),
                              int(num_tokens), _ptr(out), _stream(cache)))

@@ -457,6 +457,37 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* s, int32_t max
   return ok();
 }
 
+gqa_status gqa_kv_copy_blocks(const gqa_paged_shape* s, void* k_cache, void* v_cache,
+                              float* k_scale, float* v_scale, const int32_t* src_blocks,
+                              const int32_t* dst_blocks, int32_t num_pairs, hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (num_pairs < 0 || num_pairs > INT32_MAX / 2)
+    return fail(GQA_ERR_INVALID_ARG, "num_pairs %d out of range", num_pairs);
+  const bool fp8 = s->kv_dtype == GQA_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
+    return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale are required for fp8 pools and must be "
+                "NULL for bf16");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks)
+    return fail(GQA_ERR_INVALID_ARG, "copy_blocks: NULL device pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(GQA_ERR_INVALID_ARG, "copy_blocks: pools must be 16-byte aligned");
+  gqa::CopyBlocksParams p;
+  p.k_cache = static_cast<char*>(k_cache);
+  p.v_cache = static_cast<char*>(v_cache);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.src = src_blocks;
+  p.dst = dst_blocks;
+  p.num_kv_heads = s->num_kv_heads;
+  p.num_blocks = s->num_blocks;
+  p.tile_bytes = s->block_size * s->head_dim * (fp8 ? 1 : 2);
+  st = launch(reinterpret_cast<const void*>(&gqa::kv_copy_blocks_kernel),
+              dim3(num_pairs, s->num_kv_heads), dim3(256), &p, "kv_copy_blocks", stream);
+  return st == GQA_OK ? ok() : st;
+}
+
 gqa_status gqa_kv_gather(const gqa_paged_shape* s, const void* cache, const int32_t* block_tables,
                          int32_t seq, int32_t num_tokens, void* out, hipStream_t stream) {
   gqa_status st = check_shape(s);

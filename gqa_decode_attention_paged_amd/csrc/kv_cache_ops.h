@@ -1,4 +1,5 @@
-// KV append (commit new tokens of each sequence) and a block-table gather.
+// KV append (commit new tokens of each sequence), the copy-on-write block copy,
+// and a block-table gather.
 //
 // Cites: *LLM Inference Systems Engineering* (jasonzhang109) §2.1.3 — a decode
 // step first writes the pending token's K/V into the cache, then attends;
@@ -7,7 +8,12 @@
 // (wrwei.github.io), "Mapping logical positions to physical blocks" — token t
 // lives in physical block table[t / BS] at slot t % BS.
 //
-// Both are plain byte copies in 16-byte units (bit-exact).
+// Copy-on-write: *Module 10*, "Share only state with the same identity" — a
+// sequence about to write into a shared block that is not yet full first gets a
+// private copy; *The Mathematics of Transformer Inference* §9 (reference counts
+// and copy-on-write).
+//
+// All are plain byte copies in 16-byte units (bit-exact).
 #pragma once
 
 #include "common.h"
@@ -47,6 +53,41 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
     const size_t dst = (((size_t)blk * p.num_kv_heads + h) * p.block_size + slot) * p.head_dim + c * 8;
     *reinterpret_cast<uint4*>(p.k_cache + dst) = *reinterpret_cast<const uint4*>(p.k_new + src);
     *reinterpret_cast<uint4*>(p.v_cache + dst) = *reinterpret_cast<const uint4*>(p.v_new + src);
+  }
+}
+
+struct CopyBlocksParams {
+  char* k_cache;                // [NB][Hkv][BS][row_bytes]
+  char* v_cache;
+  float* k_scale;               // [NB][Hkv] fp8 scales, or null
+  float* v_scale;
+  const int32_t* src;           // [num_pairs] source block ids
+  const int32_t* dst;           // [num_pairs] destination block ids
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t tile_bytes;           // BS * row_bytes, a multiple of 16
+};
+
+// grid: (num_pairs, Hkv); 256 threads copy one (block, KV head) tile of K and
+// of V.  Pairs with an id outside the pool, or src == dst, copy nothing.
+__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(CopyBlocksParams p) {
+  const int src = p.src[blockIdx.x];
+  const int dst = p.dst[blockIdx.x];
+  if ((unsigned)src >= (unsigned)p.num_blocks || (unsigned)dst >= (unsigned)p.num_blocks ||
+      src == dst)
+    return;
+  const size_t h = blockIdx.y;
+  const size_t so = ((size_t)src * p.num_kv_heads + h) * p.tile_bytes;
+  const size_t dof = ((size_t)dst * p.num_kv_heads + h) * p.tile_bytes;
+  for (int u = threadIdx.x; u < p.tile_bytes / 16; u += blockDim.x) {
+    *reinterpret_cast<uint4*>(p.k_cache + dof + (size_t)u * 16) =
+        *reinterpret_cast<const uint4*>(p.k_cache + so + (size_t)u * 16);
+    *reinterpret_cast<uint4*>(p.v_cache + dof + (size_t)u * 16) =
+        *reinterpret_cast<const uint4*>(p.v_cache + so + (size_t)u * 16);
+  }
+  if (p.k_scale && threadIdx.x == 0) {
+    p.k_scale[(size_t)dst * p.num_kv_heads + h] = p.k_scale[(size_t)src * p.num_kv_heads + h];
+    p.v_scale[(size_t)dst * p.num_kv_heads + h] = p.v_scale[(size_t)src * p.num_kv_heads + h];
   }
 }
 

@@ -302,6 +302,27 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t
                                            hipStream_t stream);
 
 /*
+ * gqa_kv_copy_blocks — the copy-on-write block copy: for j < num_pairs, block
+ * dst_blocks[j] of both pools becomes a bit-exact copy of block src_blocks[j]
+ * (every KV head and slot, K and V, and for fp8 pools the per-(block, head)
+ * scales).  Used before a sequence writes into a block it shares with others
+ * (reference counting and table updates are the caller's).
+ *   k_cache, v_cache  pools, modified in place at the destination blocks
+ *   k_scale, v_scale  [num_blocks][H_kv] fp32 for fp8 pools (copied along);
+ *                 must be NULL for bf16
+ *   src_blocks, dst_blocks  [num_pairs] int32 device arrays; a pair with an id
+ *                 outside [0, num_blocks), or with src == dst, copies nothing
+ * Precondition: no block is the destination of two pairs or both a source and
+ * a destination in one call (the copies run concurrently).
+ * Cites: *Module 10*, "Share only state with the same identity"; *Stochastic
+ * Parrot* vol. 1 ch. 6 §6.4; *The Mathematics of Transformer Inference* §9.
+ */
+gqa_status gqa_kv_copy_blocks(const gqa_paged_shape* shape, void* k_cache, void* v_cache,
+                              float* k_scale, float* v_scale,
+                              const int32_t* src_blocks, const int32_t* dst_blocks,
+                              int32_t num_pairs, hipStream_t stream);
+
+/*
  * gqa_kv_gather — copy the first num_tokens cached rows of sequence `seq` out
  * of one pool into a contiguous [H_kv][num_tokens][d_h] array (element width
  * of the pool), in logical order.  A bit-exact indexing check of the paged

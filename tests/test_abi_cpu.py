@@ -174,3 +174,16 @@ def test_gather_validation(lib):
 
 def test_version(lib):
     assert b"gfx950" in lib.gqa_version()
+
+
+def test_copy_blocks_validation(lib):
+    P = ctypes.c_void_p
+    s = _shape()
+    cb = lib.gqa_kv_copy_blocks
+    assert cb(ctypes.byref(s), P(16), P(16), None, None, P(16), P(16), -1, None) == 1
+    assert cb(ctypes.byref(s), P(16), P(16), P(16), P(16), P(16), P(16), 1, None) == 1
+    assert cb(ctypes.byref(s), None, P(16), None, None, P(16), P(16), 3, None) == 1
+    assert cb(ctypes.byref(s), P(16), P(16), None, None, None, None, 0, None) == 0
+    f = _shape(kv_dtype=1)
+    assert cb(ctypes.byref(f), P(16), P(16), None, None, P(16), P(16), 1, None) == 1
+    assert cb(ctypes.byref(f), P(16), P(16), P(16), None, P(16), P(16), 1, None) == 1
