@@ -13,8 +13,12 @@ checked by eye against the pages it cites:
   block copy, as integer indexing.
 * ``multi_query.paged_multi_query_attention`` — several consecutive query
   positions per sequence (speculative verification), each attending causally.
-* ``fp8.decode_e4m3fn`` — OCP FP8 E4M3 (finite-only, max 448) decoding from the
-  format definition.
+* ``fp8.decode_e4m3fn`` / ``fp8.encode_e4m3fn`` — OCP FP8 E4M3 (finite-only,
+  max 448) decoding from the format definition, and encoding as a nearest-value
+  search with ties to even.
+* ``quant_cache.kv_append_fp8`` — appending tokens to an fp8 cache with one
+  scale per (block, KV head), the scale growing (and older codes re-encoded)
+  when new tokens exceed it.
 * ``online.chunked_attention`` / ``online.merge_partials`` — the online-softmax
   block update and the log-sum-exp merge of partial results, in the pages' own
   steps, to pin the split decomposition against the direct form.
@@ -27,7 +31,8 @@ values printed on the pages).  No function here is "parity unpinned".
 from .attention import paged_decode_attention, dense_decode_attention
 from .cache import kv_append, kv_append_tokens, gather_sequence, copy_blocks
 from .multi_query import paged_multi_query_attention
-from .fp8 import decode_e4m3fn
+from .fp8 import decode_e4m3fn, encode_e4m3fn
+from .quant_cache import kv_append_fp8
 from .bf16 import bf16_to_float64
 from .online import chunked_attention, merge_partials
 from .formulas import kv_cache_bytes, decode_attention_flops, decode_attention_intensity
@@ -35,6 +40,6 @@ from .formulas import kv_cache_bytes, decode_attention_flops, decode_attention_i
 __all__ = [
     "paged_decode_attention", "dense_decode_attention", "kv_append", "kv_append_tokens",
     "gather_sequence", "copy_blocks", "paged_multi_query_attention",
-    "decode_e4m3fn", "bf16_to_float64", "chunked_attention", "merge_partials",
+    "decode_e4m3fn", "encode_e4m3fn", "kv_append_fp8", "bf16_to_float64", "chunked_attention", "merge_partials",
     "kv_cache_bytes", "decode_attention_flops", "decode_attention_intensity",
 ]
