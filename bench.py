@@ -16,6 +16,10 @@ Workload ``verify4`` is the verification pass of speculative decoding on the
 8K grouped-query shape: each step commits 4 new tokens (the pending one and 3
 drafts) and attends for all 4 positions, in one fused kernel.
 
+Workload ``mha_fp8_append`` is the fp8 decode step on the 40-head MHA shape:
+the quantising append of each sequence's new token (power-of-two scale per
+(block, KV head), grown if needed) fused with fp8 attention, one launch.
+
 Workload ``cow_fork`` measures the copy-on-write block copy instead: 256 prompts
 on the 8K grouped-query pool geometry each fork into 8 parallel samples, so each
 prompt's partially filled last block is copied to 7 fresh blocks (1792 copies,
@@ -167,9 +171,15 @@ def cpu_baseline(case, kv_bytes, min_seconds):
     n, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
         while True:
-            fn(case["q"], case["k_pool_full"], case["v_pool_full"], case["block_tables"],
+            kp, vp, ks, vs = (case["k_pool_full"], case["v_pool_full"], case["k_scale"],
+                              case["v_scale"])
+            if "fp8_k_new" in case:
+                kp, vp, ks, vs = oracle.kv_append_fp8(kp, vp, ks, vs, case["fp8_k_new"],
+                                                      case["fp8_v_new"], case["block_tables"],
+                                                      case["fp8_start"], spec.block_size)
+            fn(case["q"], kp, vp, case["block_tables"],
                case["context_lens"], spec.block_size, case["softmax_scale"], spec.kv_dtype,
-               case["k_scale"], case["v_scale"])
+               ks, vs)
             n += 1
             el = time.perf_counter() - t0
             if el >= min_seconds:
@@ -178,6 +188,7 @@ def cpu_baseline(case, kv_bytes, min_seconds):
     return {"value": round(kv_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{n} whole step(s) of the {spec.name} workload"
+                      f"{' with the fp8 append' if 'fp8_k_new' in case else ''}"
                       f"{' with %d query positions' % case['num_queries'] if case.get('num_queries') else ''}"
                       ", float64 numpy oracle, "
                       f"1 BLAS thread, {el:.1f} s total ({per_step * 1e3:.1f} ms/step)"}
@@ -190,7 +201,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b",
                     choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4",
-                             "cow_fork"])
+                             "mha_fp8_append", "cow_fork"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,12 +222,15 @@ def main():
     import numpy as np
 
     verify = args.workload == "verify4"          # 4 query positions on the 8K shape
+    fp8_append = args.workload == "mha_fp8_append"
+    base_name = {"verify4": "llama8b", "mha_fp8_append": "mha_fp8"}.get(args.workload,
+                                                                        args.workload)
     if args.traffic_from and args.workload == "cow_fork":
         write_traffic(args.workload, args.traffic_from, fork_geometry()[5])
         return
     if args.traffic_from:
         from workloads import make_case, SPECS
-        spec = SPECS["llama8b" if verify else args.workload]
+        spec = SPECS[base_name]
         write_traffic(args.workload, args.traffic_from,
                       kv_bytes_per_step(spec, make_case(spec, seed=args.seed)["context_lens"]))
         return
@@ -224,7 +238,7 @@ def main():
     import torch
 
     import gqa_decode_attention_paged_amd as gqa
-    from workloads import make_case, make_multi_query_case, SPECS
+    from workloads import make_case, make_multi_query_case, new_token_rows, SPECS
 
     if args.copy_calibration:
         # A plain elementwise kernel that reads and writes COPY_BYTES each: the known
@@ -242,9 +256,13 @@ def main():
         print(json.dumps(bench_block_copy(args, np, torch, gqa)), flush=True)
         return
     dev = torch.device("cuda:0")
-    spec = SPECS["llama8b" if verify else args.workload]
+    spec = SPECS[base_name]
     case = (make_multi_query_case(spec, 4, seed=args.seed) if verify
             else make_case(spec, seed=args.seed))
+    if fp8_append:
+        case["fp8_k_new"] = new_token_rows(spec, 1, seed=args.seed)
+        case["fp8_v_new"] = new_token_rows(spec, 1, seed=args.seed + 1)
+        case["fp8_start"] = (case["context_lens"] - 1).astype(np.int32)
     nq = case.get("num_queries", 1)
     kv_bytes = kv_bytes_per_step(spec, case["context_lens"])
 
@@ -265,6 +283,10 @@ def main():
     k0, v0 = pool(case["k_pool"]), pool(case["v_pool"])
     copies = min(256, max(1, math.ceil(ROTATE_BYTES / kv_bytes) + 1))
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    if fp8_append:                 # each pool copy has its own scales: the append writes them
+        scales = [(ks, vs)] + [(ks.clone(), vs.clone()) for _ in range(copies - 1)]
+        k8_new, v8_new = bf16(case["fp8_k_new"][:, 0]), bf16(case["fp8_v_new"][:, 0])
+        start8 = torch.from_numpy(case["fp8_start"]).to(dev)
     max_ctx = int(case["context_lens"].max())
     shape = gqa.make_shape(spec.num_seqs, spec.num_q_heads, k0, bt)
     ws = torch.zeros(max(16, gqa.multi_query_workspace_size(shape, nq, max_ctx)),
@@ -276,7 +298,12 @@ def main():
 
     def step(i):
         kc, vc = pools[i % copies]
-        if verify:                 # fused: commit the 4 new tokens, attend for all 4 positions
+        if fp8_append:             # fused: quantise and commit the new token, attend
+            ksc, vsc = scales[i % copies]
+            gqa.paged_decode_append_attention(q, k8_new, v8_new, start8, kc, vc, bt, ctx,
+                                              max_ctx, scale, out=out, out_lse=lse,
+                                              workspace=ws, k_scale=ksc, v_scale=vsc)
+        elif verify:               # fused: commit the 4 new tokens, attend for all 4 positions
             gqa.paged_decode_multi_query_append(q, k_new, v_new, kc, vc, bt, ctx, max_ctx, scale,
                                                 out=out, out_lse=lse, workspace=ws)
         elif k_new is not None:    # fused: commit the new token and attend, one kernel
@@ -288,7 +315,10 @@ def main():
 
     ms_per_step, call_ms, graphed = _timed(torch, args, step)
     achieved = kv_bytes / (call_ms * 1e-3) / 1e9
-    if verify:
+    if fp8_append:
+        kernel = ("paged_decode_kernel (fused fp8 KV append with the power-of-two scale "
+                  "policy + split attention + log-sum-exp merge)")
+    elif verify:
         kernel = ("paged_decode_kernel (fused 4-token KV append + 4 query positions, split "
                   "attention + log-sum-exp merge)")
     elif k_new is not None:
@@ -315,7 +345,7 @@ def main():
             "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
             "block_size": spec.block_size, "kv_dtype": spec.kv_dtype,
             "context_lens_total": int(case["context_lens"].sum()), "append": spec.append,
-            "query_positions": nq,
+            "query_positions": nq, "fp8_append": fp8_append,
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
         },
         "roofline": {

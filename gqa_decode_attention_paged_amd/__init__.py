@@ -74,8 +74,9 @@ def load():
                                                  ctypes.c_size_t, _P]
     lib.gqa_paged_decode_multi_query.restype = ctypes.c_int
     lib.gqa_paged_decode_multi_query_append.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P,
-                                                        _P, _P, ctypes.c_int32, ctypes.c_float,
-                                                        _P, _P, _P, ctypes.c_size_t, _P]
+                                                        _P, _P, _P, _P, ctypes.c_int32,
+                                                        ctypes.c_float, _P, _P, _P,
+                                                        ctypes.c_size_t, _P]
     lib.gqa_paged_decode_multi_query_append.restype = ctypes.c_int
     lib.gqa_decode_num_splits.argtypes = [ctypes.c_int32]
     lib.gqa_decode_num_splits.restype = ctypes.c_int32
@@ -84,12 +85,14 @@ def load():
     lib.gqa_paged_decode_attention.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
     lib.gqa_paged_decode_attention.restype = ctypes.c_int
-    lib.gqa_paged_decode_append_attention.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P,
-                                                      ctypes.c_int32, ctypes.c_float, _P, _P,
-                                                      _P, ctypes.c_size_t, _P]
+    lib.gqa_paged_decode_append_attention.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                      _P, ctypes.c_int32, ctypes.c_float, _P,
+                                                      _P, _P, ctypes.c_size_t, _P]
     lib.gqa_paged_decode_append_attention.restype = ctypes.c_int
     lib.gqa_paged_decode_workspace_init.argtypes = [S, ctypes.c_int32, _P, ctypes.c_size_t, _P]
     lib.gqa_paged_decode_workspace_init.restype = ctypes.c_int
+    lib.gqa_kv_append_fp8.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.gqa_kv_append_fp8.restype = ctypes.c_int
     lib.gqa_kv_copy_blocks.argtypes = [S, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
     lib.gqa_kv_copy_blocks.restype = ctypes.c_int
     lib.gqa_kv_gather.argtypes = [S, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]
@@ -228,9 +231,11 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
 def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tables,
                                     context_lens, max_context_len, softmax_scale=None, out=None,
                                     out_lse=None, workspace=None, return_lse=True,
-                                    batch_invariant=False, sliding_window=0):
+                                    batch_invariant=False, sliding_window=0, k_scale=None,
+                                    v_scale=None):
     """Fused verification step: commit k_new/v_new [B][Q][H_kv][d_h] at positions
-    context_lens[b] - Q + i, then attend for the Q positions (one kernel)."""
+    context_lens[b] - Q + i, then attend for the Q positions (one kernel).  fp8
+    pools: the rows are quantised into them and k_scale/v_scale updated."""
     import torch
     lib = load()
     B, Q, Hq, D = q.shape
@@ -246,7 +251,8 @@ def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tab
         workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     _check(lib.gqa_paged_decode_multi_query_append(
         ctypes.byref(shape), int(Q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
-        _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+        int(max_context_len),
         float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q)))
     return out, out_lse
@@ -262,8 +268,10 @@ def make_workspace(shape: PagedShape, max_context_len: int, device):
 def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, block_tables,
                                   context_lens, max_context_len, softmax_scale=None, out=None,
                                   out_lse=None, workspace=None, return_lse=True,
-                                  batch_invariant=False, sliding_window=0):
-    """Fused decode step: commit the new token at positions[b], then attend (one kernel)."""
+                                  batch_invariant=False, sliding_window=0, k_scale=None,
+                                  v_scale=None):
+    """Fused decode step: commit the new token at positions[b], then attend (one kernel).
+    fp8 pools: the row is quantised into them and k_scale/v_scale updated."""
     import torch
     lib = load()
     B, Hq, D = q.shape
@@ -278,7 +286,8 @@ def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, 
         workspace = make_workspace(shape, max_context_len, q.device)
     _check(lib.gqa_paged_decode_append_attention(
         ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(k_cache),
-        _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+        int(max_context_len),
         float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q)))
     return out, out_lse
@@ -289,6 +298,21 @@ def workspace_init(shape: PagedShape, max_context_len: int, workspace):
     _check(load().gqa_paged_decode_workspace_init(
         ctypes.byref(shape), int(max_context_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(workspace)))
+
+
+def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                  start_positions):
+    """Quantise and write new tokens into an fp8 pool with per-(block, KV head)
+    scales: k_new/v_new bf16 [B][H_kv][d_h] (one token) or [B][T][H_kv][d_h] at
+    positions start_positions[b] + j (in place, scales included)."""
+    lib = load()
+    if k_new.dim() == 3:
+        k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
+    B, T = k_new.shape[0], k_new.shape[1]
+    shape = make_shape(B, k_cache.shape[1], k_cache, block_tables)
+    _check(lib.gqa_kv_append_fp8(ctypes.byref(shape), int(T), _ptr(k_new), _ptr(v_new),
+                                 _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                 _ptr(block_tables), _ptr(start_positions), _stream(k_cache)))
 
 
 def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_scale=None):

@@ -58,6 +58,71 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out) {
   out[3] = hi[1];
 }
 
+constexpr float kFp8Max = 448.0f;
+
+// The smallest power of two >= t, for finite t >= 0 (0 stays 0).
+__device__ __forceinline__ float pow2_ceil(float t) {
+  const uint32_t u = __float_as_uint(t);
+  if ((u & 0x7fffffu) == 0) return t;
+  return __uint_as_float((u & 0x7f800000u) + 0x800000u);
+}
+
+// Four values -> four E4M3 codes of clamp(x / s, -448, 448) in one word (s == 0:
+// zeros).  One IEEE fp32 division per value; the gfx950 converter rounds to
+// nearest even.
+__device__ __forceinline__ uint32_t encode4_e4m3(const float* x, float s) {
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = s > 0.f ? __builtin_fminf(__builtin_fmaxf(x[i] / s, -kFp8Max), kFp8Max) : 0.f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// One wave appends n new bf16 rows (row j at rows + j * row_stride) to slots
+// first .. first + n - 1 of one E4M3 (block, KV head) tile with its scale:
+// t = max|new| / 448; a block opening here (first == 0) takes pow2_ceil(t); one
+// holding older tokens keeps its scale when that is >= t, else takes
+// pow2_ceil(t) and re-encodes its older codes as encode(decode(c) * old / s).
+// Returns the new scale (the same in every lane).
+__device__ __forceinline__ float wave_append_fp8(uint8_t* tile, float* scale_ptr, int first, int n,
+                                                 const uint16_t* rows, size_t row_stride, int D,
+                                                 int lane) {
+  const int quads = D / 4;
+  float am = 0.f;
+  for (int e = lane; e < n * quads; e += kWave) {
+    const uint2 w = *reinterpret_cast<const uint2*>(rows + (size_t)(e / quads) * row_stride +
+                                                    (e % quads) * 4);
+    am = __builtin_fmaxf(am, __builtin_fmaxf(
+        __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.x)), __builtin_fabsf(bf16_hi(w.x))),
+        __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.y)), __builtin_fabsf(bf16_hi(w.y)))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, o));
+  const float old = *scale_ptr;
+  const float t = am / kFp8Max;
+  const float s = (first > 0 && old >= t) ? old : pow2_ceil(t);
+  uint32_t* w32 = reinterpret_cast<uint32_t*>(tile);
+  if (first > 0 && t > old) {
+    for (int e = lane; e < first * quads; e += kWave) {
+      float v[4];
+      fp8x4_to_f32(w32[e], v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = v[i] * old;
+      w32[e] = encode4_e4m3(v, s);
+    }
+  }
+  for (int e = lane; e < n * quads; e += kWave) {
+    const int j = e / quads, c = e % quads;
+    const uint2 w = *reinterpret_cast<const uint2*>(rows + (size_t)j * row_stride + c * 4);
+    const float v[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+    w32[(size_t)(first + j) * quads + c] = encode4_e4m3(v, s);
+  }
+  if (lane == 0) *scale_ptr = s;
+  return s;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kNegInf = -__builtin_huge_valf();

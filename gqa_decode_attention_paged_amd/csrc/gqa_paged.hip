@@ -288,6 +288,44 @@ gqa_status gqa_kv_append_tokens(const gqa_paged_shape* s, int32_t num_tokens, co
                      stream);
 }
 
+gqa_status gqa_kv_append_fp8(const gqa_paged_shape* s, int32_t num_tokens, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache, float* k_scale,
+                             float* v_scale, const int32_t* block_tables,
+                             const int32_t* start_positions, hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (num_tokens < 0 || num_tokens > 65535)
+    return fail(GQA_ERR_INVALID_ARG, "num_tokens %d outside [0, 65535]", num_tokens);
+  if (s->kv_dtype != GQA_KV_FP8_E4M3)
+    return fail(GQA_ERR_INVALID_ARG, "kv_append_fp8 needs an fp8 pool (use kv_append for bf16)");
+  if (s->num_seqs == 0 || num_tokens == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+      !start_positions)
+    return fail(GQA_ERR_INVALID_ARG, "kv_append_fp8: NULL device pointer");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(GQA_ERR_INVALID_ARG, "kv_append_fp8: K/V pointers must be 16-byte aligned");
+  if (s->num_kv_heads > 65535)
+    return fail(GQA_ERR_UNSUPPORTED, "kv_append_fp8: num_kv_heads %d > 65535", s->num_kv_heads);
+  gqa::AppendFp8Params p;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.start = start_positions;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = s->num_kv_heads;
+  p.head_dim = s->head_dim;
+  p.block_size = s->block_size;
+  p.num_blocks = s->num_blocks;
+  p.max_blocks = s->max_blocks_per_seq;
+  st = launch(reinterpret_cast<const void*>(&gqa::kv_append_fp8_kernel),
+              dim3(s->num_seqs, s->num_kv_heads, 2), dim3(256), &p, "kv_append_fp8", stream);
+  return st == GQA_OK ? ok() : st;
+}
+
 static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, const void* q,
                               void* k_cache,
                               void* v_cache, const float* k_scale, const float* v_scale,
@@ -310,14 +348,15 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
     return fail(GQA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
   if (!fp8 && (k_scale || v_scale))
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
-  if ((positions || append_tail) && fp8)
-    return fail(GQA_ERR_UNSUPPORTED, "the fused append supports bf16 pools only");
   const int G = s->num_q_heads / s->num_kv_heads;
   if (num_queries < 1) return fail(GQA_ERR_INVALID_ARG, "num_queries %d < 1", num_queries);
   if ((int64_t)G * num_queries > (fp8 ? kMaxRowsFp8 : kMaxRowsBf16))
     return fail(GQA_ERR_UNSUPPORTED, "G * num_queries = %lld rows exceeds %d for this KV dtype",
                 (long long)G * num_queries, fp8 ? kMaxRowsFp8 : kMaxRowsBf16);
   const int rows = G * num_queries;
+  if (append_tail && num_queries > s->block_size)
+    return fail(GQA_ERR_UNSUPPORTED, "the fused append takes at most block_size (%d) tokens",
+                s->block_size);
   if (s->num_seqs == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(GQA_ERR_INVALID_ARG, "decode: NULL device pointer");
@@ -351,8 +390,9 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = k_cache;
   p.v_cache = v_cache;
-  p.k_scale = k_scale;
-  p.v_scale = v_scale;
+  // Written only by a fused fp8 append, whose entry points take them non-const.
+  p.k_scale = const_cast<float*>(k_scale);
+  p.v_scale = const_cast<float*>(v_scale);
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.k_new = static_cast<const uint16_t*>(k_new);
@@ -411,22 +451,24 @@ gqa_status gqa_paged_decode_multi_query(const gqa_paged_shape* s, int32_t num_qu
 
 gqa_status gqa_paged_decode_multi_query_append(
     const gqa_paged_shape* s, int32_t num_queries, const void* q, const void* k_new,
-    const void* v_new, void* k_cache, void* v_cache, const int32_t* block_tables,
-    const int32_t* context_lens, int32_t max_context_len, float softmax_scale, float* out,
-    float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl(s, num_queries, q, k_cache, v_cache, nullptr, nullptr, k_new, v_new,
+    const void* v_new, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t max_context_len,
+    float softmax_scale, float* out, float* out_lse, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  return decode_impl(s, num_queries, q, k_cache, v_cache, k_scale, v_scale, k_new, v_new,
                      nullptr, block_tables, context_lens, max_context_len, softmax_scale, out,
                      out_lse, workspace, workspace_bytes, stream, true);
 }
 
 gqa_status gqa_paged_decode_append_attention(
     const gqa_paged_shape* s, const void* q, const void* k_new, const void* v_new,
-    const int32_t* positions, void* k_cache, void* v_cache, const int32_t* block_tables,
-    const int32_t* context_lens, int32_t max_context_len, float softmax_scale, float* out,
-    float* out_lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int32_t* positions, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t max_context_len,
+    float softmax_scale, float* out, float* out_lse, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
   if (s && s->num_seqs > 0 && !positions)
     return fail(GQA_ERR_INVALID_ARG, "append: NULL positions");
-  return decode_impl(s, 1, q, k_cache, v_cache, nullptr, nullptr, k_new, v_new, positions,
+  return decode_impl(s, 1, q, k_cache, v_cache, k_scale, v_scale, k_new, v_new, positions,
                      block_tables, context_lens, max_context_len, softmax_scale, out, out_lse,
                      workspace, workspace_bytes, stream);
 }
@@ -480,11 +522,16 @@ gqa_status gqa_kv_copy_blocks(const gqa_paged_shape* s, void* k_cache, void* v_c
   p.v_scale = v_scale;
   p.src = src_blocks;
   p.dst = dst_blocks;
-  p.num_kv_heads = s->num_kv_heads;
   p.num_blocks = s->num_blocks;
-  p.tile_bytes = s->block_size * s->head_dim * (fp8 ? 1 : 2);
+  p.num_kv_heads = s->num_kv_heads;
+  p.block_bytes = (int64_t)s->num_kv_heads * s->block_size * s->head_dim * (fp8 ? 1 : 2);
+  const int64_t slices = (p.block_bytes + gqa::kCopySliceBytes - 1) / gqa::kCopySliceBytes;
+  if (slices > 65535)
+    return fail(GQA_ERR_INVALID_ARG, "copy_blocks: block of %lld bytes is too large",
+                (long long)p.block_bytes);
   st = launch(reinterpret_cast<const void*>(&gqa::kv_copy_blocks_kernel),
-              dim3(num_pairs, s->num_kv_heads), dim3(256), &p, "kv_copy_blocks", stream);
+              dim3(num_pairs, (unsigned)slices), dim3(gqa::kCopyThreads), &p, "kv_copy_blocks",
+              stream);
   return st == GQA_OK ? ok() : st;
 }
 

@@ -13,7 +13,11 @@
 // private copy; *The Mathematics of Transformer Inference* §9 (reference counts
 // and copy-on-write).
 //
-// All are plain byte copies in 16-byte units (bit-exact).
+// The bf16 append, the copy and the gather are plain byte copies in 16-byte
+// units (bit-exact).  The fp8 append quantises: *The Mathematics of Transformer
+// Inference* §11 (x ~ s * round(x / s), KV scales per head and per token,
+// dequantisation fused into attention); the E4M3 code and its largest value
+// 448 as in *Module 10*'s number-format table.
 #pragma once
 
 #include "common.h"
@@ -56,38 +60,142 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   }
 }
 
+struct AppendFp8Params {
+  const uint16_t* k_new;        // [B][T][Hkv][D] bf16
+  const uint16_t* v_new;
+  uint8_t* k_cache;             // [NB][Hkv][BS][D] E4M3 codes
+  uint8_t* v_cache;
+  float* k_scale;               // [NB][Hkv]
+  float* v_scale;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* start;         // [B]: positions start[b] .. start[b] + T - 1; < 0: none
+  int32_t num_tokens;           // T
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks;
+};
+
+__device__ __forceinline__ float workgroup_max256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// grid: (B, Hkv, 2), 256 threads; z = 0 writes K, z = 1 writes V.  The workgroup
+// walks the blocks its sequence's T new tokens fall in.  Per (block, head) tile,
+// with `first` the lowest slot written and t = amax(new rows) / 448:
+//   first == 0 (the block opens):   s = pow2_ceil(t)
+//   first > 0, old scale >= t:      s = old (older codes untouched)
+//   first > 0, old scale <  t:      s = pow2_ceil(t); older codes re-encoded as
+//                                   encode(decode(c) * old / s)
+// then the new rows are encode(x / s) and the tile's scale becomes s.  Scales
+// are powers of two, so a re-encode only shifts exponents (exact while values
+// stay normal E4M3).
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendFp8Params p) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const uint16_t* xnew = is_v ? p.v_new : p.k_new;
+  uint8_t* pool = is_v ? p.v_cache : p.k_cache;
+  float* scales = is_v ? p.v_scale : p.k_scale;
+  const int st = p.start[b];
+  if (st < 0) return;
+  const int BS = p.block_size, D = p.head_dim, quads = D / 4;
+  const int64_t end = (int64_t)st + p.num_tokens;
+  const size_t row_stride = (size_t)p.num_kv_heads * D;         // between tokens of k_new
+  for (int64_t pos = st; pos < end;) {
+    const int64_t bi = pos / BS;
+    const int first = (int)(pos % BS);
+    const int n = (int)(end - pos < BS - first ? end - pos : BS - first);
+    if (bi >= p.max_blocks) break;
+    const int blk = p.block_tables[(size_t)b * p.max_blocks + bi];
+    if ((unsigned)blk < (unsigned)p.num_blocks) {
+      const uint16_t* rows = xnew + (((size_t)b * p.num_tokens + (size_t)(pos - st)) *
+                                     p.num_kv_heads + h) * D;
+      float* sp = scales + (size_t)blk * p.num_kv_heads + h;
+      const float old = *sp;
+      float am = 0.f;
+      for (int e = threadIdx.x; e < n * quads; e += 256) {
+        const uint2 w = *reinterpret_cast<const uint2*>(rows + (size_t)(e / quads) * row_stride +
+                                                        (e % quads) * 4);
+        am = __builtin_fmaxf(am, __builtin_fmaxf(
+            __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.x)), __builtin_fabsf(bf16_hi(w.x))),
+            __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.y)), __builtin_fabsf(bf16_hi(w.y)))));
+      }
+      am = workgroup_max256(am, red);            // also orders every read of *sp before its write
+      const float t = am / kFp8Max;
+      const bool older = first > 0;
+      const float s = (older && old >= t) ? old : pow2_ceil(t);
+      uint32_t* tile = reinterpret_cast<uint32_t*>(pool + ((size_t)blk * p.num_kv_heads + h) *
+                                                   BS * D);
+      if (older && t > old) {
+        for (int e = threadIdx.x; e < first * quads; e += 256) {
+          float v[4];
+          fp8x4_to_f32(tile[e], v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = v[i] * old;
+          tile[e] = encode4_e4m3(v, s);
+        }
+      }
+      for (int e = threadIdx.x; e < n * quads; e += 256) {
+        const int j = e / quads, c = e % quads;
+        const uint2 w = *reinterpret_cast<const uint2*>(rows + (size_t)j * row_stride + c * 4);
+        const float v[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        tile[(size_t)(first + j) * quads + c] = encode4_e4m3(v, s);
+      }
+      if (threadIdx.x == 0) *sp = s;
+    }
+    pos += n;
+  }
+}
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopySliceBytes = kCopyThreads * 16;       // 4 KiB of each pool per workgroup
+
 struct CopyBlocksParams {
-  char* k_cache;                // [NB][Hkv][BS][row_bytes]
+  char* k_cache;                // [NB][Hkv][BS][row_bytes]: one block is contiguous
   char* v_cache;
   float* k_scale;               // [NB][Hkv] fp8 scales, or null
   float* v_scale;
   const int32_t* src;           // [num_pairs] source block ids
   const int32_t* dst;           // [num_pairs] destination block ids
-  int32_t num_kv_heads;
   int32_t num_blocks;
-  int32_t tile_bytes;           // BS * row_bytes, a multiple of 16
+  int32_t num_kv_heads;
+  int64_t block_bytes;          // Hkv * BS * row_bytes, a multiple of 16
 };
 
-// grid: (num_pairs, Hkv); 256 threads copy one (block, KV head) tile of K and
-// of V.  Pairs with an id outside the pool, or src == dst, copy nothing.
-__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(CopyBlocksParams p) {
+// grid: (num_pairs, ceil(block_bytes / kCopySliceBytes)); workgroup (j, s) copies
+// byte slice s of block src[j] onto block dst[j] in both pools, 16 bytes per
+// thread, and slice 0 also copies the blocks' fp8 scales.  Pairs with an id
+// outside the pool, or src == dst, copy nothing.  A fork lists one source for
+// several copies; each copy reads it again, which the caches serve: the step is
+// bound by its writes, and small workgroups keep the most stores in flight
+// (reading a shared source once for a run of copies measured slower).
+__global__ __launch_bounds__(kCopyThreads) void kv_copy_blocks_kernel(CopyBlocksParams p) {
   const int src = p.src[blockIdx.x];
   const int dst = p.dst[blockIdx.x];
   if ((unsigned)src >= (unsigned)p.num_blocks || (unsigned)dst >= (unsigned)p.num_blocks ||
       src == dst)
     return;
-  const size_t h = blockIdx.y;
-  const size_t so = ((size_t)src * p.num_kv_heads + h) * p.tile_bytes;
-  const size_t dof = ((size_t)dst * p.num_kv_heads + h) * p.tile_bytes;
-  for (int u = threadIdx.x; u < p.tile_bytes / 16; u += blockDim.x) {
-    *reinterpret_cast<uint4*>(p.k_cache + dof + (size_t)u * 16) =
-        *reinterpret_cast<const uint4*>(p.k_cache + so + (size_t)u * 16);
-    *reinterpret_cast<uint4*>(p.v_cache + dof + (size_t)u * 16) =
-        *reinterpret_cast<const uint4*>(p.v_cache + so + (size_t)u * 16);
+  const int64_t off = (int64_t)blockIdx.y * kCopySliceBytes + (int64_t)threadIdx.x * 16;
+  if (off < p.block_bytes) {
+    const uint4 kv = *reinterpret_cast<const uint4*>(p.k_cache + (size_t)src * p.block_bytes + off);
+    const uint4 vv = *reinterpret_cast<const uint4*>(p.v_cache + (size_t)src * p.block_bytes + off);
+    *reinterpret_cast<uint4*>(p.k_cache + (size_t)dst * p.block_bytes + off) = kv;
+    *reinterpret_cast<uint4*>(p.v_cache + (size_t)dst * p.block_bytes + off) = vv;
   }
-  if (p.k_scale && threadIdx.x == 0) {
-    p.k_scale[(size_t)dst * p.num_kv_heads + h] = p.k_scale[(size_t)src * p.num_kv_heads + h];
-    p.v_scale[(size_t)dst * p.num_kv_heads + h] = p.v_scale[(size_t)src * p.num_kv_heads + h];
+  if (p.k_scale && blockIdx.y == 0) {
+    for (int h = threadIdx.x; h < p.num_kv_heads; h += kCopyThreads) {
+      p.k_scale[(size_t)dst * p.num_kv_heads + h] = p.k_scale[(size_t)src * p.num_kv_heads + h];
+      p.v_scale[(size_t)dst * p.num_kv_heads + h] = p.v_scale[(size_t)src * p.num_kv_heads + h];
+    }
   }
 }
 

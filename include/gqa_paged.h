@@ -252,12 +252,16 @@ gqa_status gqa_paged_decode_multi_query(const gqa_paged_shape* shape, int32_t nu
  *   other arguments as gqa_paged_decode_multi_query (k_cache/v_cache are
  *   written at those Q slots only).  Same results as gqa_kv_append_tokens at
  *   those positions followed by gqa_paged_decode_multi_query.  A sequence with
- *   an invalid length (NaN outputs) appends nothing.  bf16 pools only.
+ *   an invalid length (NaN outputs) appends nothing.
+ *   fp8 pools: k_scale/v_scale are required and updated; the rows are
+ *   quantised as gqa_kv_append_fp8 with start = context_lens[b] - Q does
+ *   (same codes and scales), then attended.  Q <= block_size.
  */
 gqa_status gqa_paged_decode_multi_query_append(const gqa_paged_shape* shape,
                                                int32_t num_queries, const void* q,
                                                const void* k_new, const void* v_new,
                                                void* k_cache, void* v_cache,
+                                               float* k_scale, float* v_scale,
                                                const int32_t* block_tables,
                                                const int32_t* context_lens,
                                                int32_t max_context_len,
@@ -274,7 +278,9 @@ gqa_status gqa_paged_decode_multi_query_append(const gqa_paged_shape* shape,
  *                 new token (normally context_lens[b] - 1; negative = no append)
  *   other arguments as gqa_paged_decode_attention (k_cache/v_cache are written
  *   at the appended slots only).  Same results as gqa_kv_append followed by
- *   gqa_paged_decode_attention.  bf16 pools only (fp8: GQA_ERR_UNSUPPORTED).
+ *   gqa_paged_decode_attention.  fp8 pools: k_scale/v_scale (NULL for bf16)
+ *   are required and updated; the row is quantised as gqa_kv_append_fp8 with
+ *   start = positions[b] does (same codes and scales), then attended.
  * Cites: *LLM Inference Systems Engineering* §2.1.3 (each step commits the
  * pending token's K/V, then attends over the cache that includes it).
  */
@@ -283,6 +289,7 @@ gqa_status gqa_paged_decode_append_attention(const gqa_paged_shape* shape,
                                              const void* k_new, const void* v_new,
                                              const int32_t* positions,
                                              void* k_cache, void* v_cache,
+                                             float* k_scale, float* v_scale,
                                              const int32_t* block_tables,
                                              const int32_t* context_lens,
                                              int32_t max_context_len,
@@ -302,6 +309,35 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t
                                            hipStream_t stream);
 
 /*
+ * gqa_kv_append_fp8 — append num_tokens (T) new tokens per sequence to an fp8
+ * (E4M3) pool, quantising them with one fp32 scale per (block, KV head).
+ *   k_new, v_new  [num_seqs][T][H_kv][head_dim] bf16 rows, finite (as are the
+ *                 codes already in a block the call appends to)
+ *   k_cache, v_cache  [num_blocks][H_kv][block_size][head_dim] E4M3 codes, and
+ *   k_scale, v_scale  [num_blocks][H_kv] fp32 (value = decode(code) * scale):
+ *                 modified in place at the blocks written
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32
+ *   start_positions [num_seqs] int32: sequence b writes positions start[b] ..
+ *                 start[b] + T - 1 (its current length upward); start < 0: none.
+ *                 Positions past the table, or whose table entry is not a block
+ *                 of the pool, are skipped.
+ * Scale policy, per (block, KV head) tile written, with first = the lowest slot
+ * written and t = max|new value| / 448: a block opened by the call (first == 0)
+ * takes the smallest power of two >= t; a block holding older tokens keeps its
+ * scale when that is >= t, and otherwise takes the smallest power of two >= t
+ * and has its older codes re-encoded (exact while they stay normal E4M3).  New
+ * values are encoded as round-to-nearest-even of clamp(x / scale, -448, 448).
+ * Precondition: no two sequences write the same block in one call.
+ * Cites: *The Mathematics of Transformer Inference* §11 (x ~ s * round(x / s);
+ * KV scales per head, per token); *Module 10*, "Quantise the cache, evaluate
+ * the artifact" and the E4M3 row of its number-format table (largest value 448).
+ */
+gqa_status gqa_kv_append_fp8(const gqa_paged_shape* shape, int32_t num_tokens,
+                             const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             float* k_scale, float* v_scale, const int32_t* block_tables,
+                             const int32_t* start_positions, hipStream_t stream);
+
+/*
  * gqa_kv_copy_blocks — the copy-on-write block copy: for j < num_pairs, block
  * dst_blocks[j] of both pools becomes a bit-exact copy of block src_blocks[j]
  * (every KV head and slot, K and V, and for fp8 pools the per-(block, head)
@@ -312,6 +348,7 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t
  *                 must be NULL for bf16
  *   src_blocks, dst_blocks  [num_pairs] int32 device arrays; a pair with an id
  *                 outside [0, num_blocks), or with src == dst, copies nothing
+ * A source may appear in several pairs (a fork copies one block several times).
  * Precondition: no block is the destination of two pairs or both a source and
  * a destination in one call (the copies run concurrently).
  * Cites: *Module 10*, "Share only state with the same identity"; *Stochastic

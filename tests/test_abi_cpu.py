@@ -139,13 +139,18 @@ def test_zero_sequences_return_ok_without_launching(lib):
 def test_fused_append_validation(lib):
     P = ctypes.c_void_p
     s = _shape()
-    call = lambda shape, pos, kn: lib.gqa_paged_decode_append_attention(
-        ctypes.byref(shape), P(16), P(kn), P(16), P(pos), P(16), P(16), P(16), P(16), 100, 0.1,
-        P(16), None, P(16), 1 << 30, None)
+    call = lambda shape, pos, kn, sc=None: lib.gqa_paged_decode_append_attention(
+        ctypes.byref(shape), P(16), P(kn), P(16), P(pos), P(16), P(16), P(sc), P(sc), P(16),
+        P(16), 100, 0.1, P(16), None, P(16), 1 << 30, None)
     assert call(s, None, 16) == 1                     # positions required
     assert call(s, 16, None) == 1                     # new rows required
-    assert call(_shape(kv_dtype=1), 16, 16) in (1, 2)  # fp8 pools: no fused append
+    assert call(s, 16, 16, 16) == 1                   # bf16 pools take no scales
+    assert call(_shape(kv_dtype=1), 16, 16) == 1      # fp8 pools need their scales
     assert call(_shape(num_seqs=0), None, None) == 0
+    mq = lambda shape, nq: lib.gqa_paged_decode_multi_query_append(
+        ctypes.byref(shape), nq, P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16),
+        100, 0.1, P(16), None, P(16), 1 << 30, None)
+    assert mq(_shape(kv_dtype=1, num_q_heads=8, block_size=16), 17) == 2   # > block size
 
 
 def test_workspace_init_validation(lib):
@@ -187,3 +192,16 @@ def test_copy_blocks_validation(lib):
     f = _shape(kv_dtype=1)
     assert cb(ctypes.byref(f), P(16), P(16), None, None, P(16), P(16), 1, None) == 1
     assert cb(ctypes.byref(f), P(16), P(16), P(16), None, P(16), P(16), 1, None) == 1
+
+
+def test_append_fp8_validation(lib):
+    P = ctypes.c_void_p
+    ap = lib.gqa_kv_append_fp8
+    f = _shape(kv_dtype=1)
+    args = [P(16)] * 8
+    assert ap(ctypes.byref(_shape()), 1, *args, None) == 1            # bf16 pool
+    assert ap(ctypes.byref(f), -1, *args, None) == 1
+    assert ap(ctypes.byref(f), 70000, *args, None) == 1
+    assert ap(ctypes.byref(f), 0, *args, None) == 0                   # nothing to write
+    assert ap(ctypes.byref(f), 1, *([P(16)] * 4), None, P(16), P(16), P(16), None) == 1
+    assert ap(ctypes.byref(f), 1, P(8), *([P(16)] * 7), None) == 1      # misaligned rows

@@ -75,6 +75,32 @@ def test_copy_blocks_is_bit_exact(gpu, dt, hkv, bs, d, nb, n):
         assert np.array_equal(vsd.cpu().numpy(), ref[3])
 
 
+@pytest.mark.parametrize("dt,seed", [("bf16", 0), ("bf16", 1), ("fp8", 2)])
+def test_copy_blocks_with_shared_sources(gpu, dt, seed):
+    """Forks list one source several times in a row (runs of 1 to 20 copies), with
+    invalid ids inside runs: every copy is made."""
+    rng = np.random.default_rng(100 + seed)
+    nb, hkv, bs, d = 400, 8, 16, 128
+    k, v, ks, vs = _random_pool(rng, nb, hkv, bs, d, dt)
+    runs = rng.integers(1, 21, 20)
+    perm = rng.permutation(nb).astype(np.int32)
+    src = np.repeat(perm[:len(runs)], runs).astype(np.int32)
+    dst = perm[len(runs):len(runs) + len(src)].copy()
+    src[5], dst[9], dst[17] = -1, nb + 3, src[17]
+    ref = oracle.copy_blocks(k, v, src, dst, ks, vs)
+    kd, vd = _dev_pool(k), _dev_pool(v)
+    ksd = None if ks is None else torch.from_numpy(ks).to("cuda:0")
+    vsd = None if vs is None else torch.from_numpy(vs).to("cuda:0")
+    gpu.kv_copy_blocks(kd, vd, torch.from_numpy(src).to("cuda:0"),
+                       torch.from_numpy(dst).to("cuda:0"), ksd, vsd)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host_pool(kd, k.dtype), ref[0])
+    assert np.array_equal(_host_pool(vd, v.dtype), ref[1])
+    if ks is not None:
+        assert np.array_equal(ksd.cpu().numpy(), ref[2])
+        assert np.array_equal(vsd.cpu().numpy(), ref[3])
+
+
 def test_copy_no_pairs_changes_nothing(gpu):
     rng = np.random.default_rng(5)
     k, v, _, _ = _random_pool(rng, 10, 2, 16, 64, "bf16")

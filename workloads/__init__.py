@@ -294,6 +294,16 @@ def make_multi_query_case(spec: Spec | str, num_queries: int, seed: int = 0, *,
     return case
 
 
+def new_token_rows(spec: Spec | str, num_tokens: int = 1, seed: int = 0) -> np.ndarray:
+    """Seeded bf16 K or V rows of new tokens, [B][T][H_kv][d] (N(0,1) draws), for
+    appends that quantise (fp8 pools), where the pool after the append is not
+    built here."""
+    if isinstance(spec, str):
+        spec = SPECS[spec]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, spec.case_id, 2])))
+    return _normal_bf16(rng, (spec.num_seqs, num_tokens, spec.num_kv_heads, spec.head_dim))
+
+
 def _fp8_pool(rng, shape, valid):
     """N(0,1) float32 source values -> fp8 codes + per-(block, head) scale amax/448."""
     NB, H, BS, D = shape
