@@ -457,24 +457,20 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // token commits its K/V rows and waits for the stores, so its loads then read
   // the token back from the cache.  fp8 pools: the wave whose chunk holds a
   // block's first new token quantises that block's new rows (the append policy
-  // of wave_append_fp8) and invalidates its vector L1 so the re-encoded tile is
-  // read back from L2; the new scales of the (at most two, as Q <= block size)
-  // blocks are kept in registers (ablk*/aks*/avs*) and used in place of the
-  // stored ones.  When a block spans several chunks (BS > CT) other waves read
-  // it too: the scales then go through LDS and the workgroup waits for the
-  // append before any tile is read.
-  int ablk0 = -1, ablk1 = -1;
-  float aks0 = 0.f, aks1 = 0.f, avs0 = 0.f, avs1 = 0.f;
+  // of wave_append_fp8: its scale may grow and its older codes be re-encoded),
+  // waits for the stores and invalidates the CU's vector L1, so every later
+  // vector load of the tile or of its scale (buffer loads, both) reads them
+  // from L2.  When a block spans several chunks (BS > CT) other waves read it
+  // too, and the workgroup waits for the append before any tile is read.
   if constexpr (FP8) {
     constexpr bool kShared = BS > CT;
-    __shared__ float sm_ascale[2][2];
     const int na = p.append_tail ? Q : (pos >= 0 ? 1 : 0);
     const int a0 = p.append_tail ? ctx - Q : pos;
     const int rows_per_seq = p.append_tail ? Q : 1;
     const size_t stride = (size_t)p.num_kv_heads * D;
     bool wrote = false, any_here = false;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 2; ++k) {                         // at most two blocks: Q <= BS
       const int nxt = (a0 / BS + 1) * BS;                   // start of the second block
       const int lo = k == 0 ? a0 : nxt;                    // new tokens lo .. hi-1
       const int hi = k == 0 ? min(a0 + na, nxt) : a0 + na;
@@ -482,40 +478,22 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       const int blk = bt[lo / BS];
       if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
       any_here = true;
-      const bool mine = ((lo - s0) / CT) % WAVES == wave;
-      float ksn = 0.f, vsn = 0.f;
-      if (mine) {
-        const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * BS * D;
-        const size_t row = (((size_t)b * rows_per_seq + (lo - a0)) * p.num_kv_heads + kvh) * D;
-        const size_t sidx = (size_t)blk * p.num_kv_heads + kvh;
-        ksn = wave_append_fp8(static_cast<uint8_t*>(p.k_cache) + tile, p.k_scale + sidx, lo % BS,
-                              hi - lo, p.k_new + row, stride, D, lane);
-        vsn = wave_append_fp8(static_cast<uint8_t*>(p.v_cache) + tile, p.v_scale + sidx, lo % BS,
-                              hi - lo, p.v_new + row, stride, D, lane);
-        wrote = true;
-        if (kShared && lane == 0) {
-          sm_ascale[k][0] = ksn;
-          sm_ascale[k][1] = vsn;
-        }
-      }
-      if (kShared || mine) {
-        if (k == 0) {
-          ablk0 = blk; aks0 = ksn; avs0 = vsn;
-        } else {
-          ablk1 = blk; aks1 = ksn; avs1 = vsn;
-        }
-      }
+      if (((lo - s0) / CT) % WAVES != wave) continue;
+      const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * BS * D;
+      const size_t row = (((size_t)b * rows_per_seq + (lo - a0)) * p.num_kv_heads + kvh) * D;
+      const size_t sidx = (size_t)blk * p.num_kv_heads + kvh;
+      wave_append_fp8(static_cast<uint8_t*>(p.k_cache) + tile, p.k_scale + sidx, lo % BS,
+                      hi - lo, p.k_new + row, stride, D, lane);
+      wave_append_fp8(static_cast<uint8_t*>(p.v_cache) + tile, p.v_scale + sidx, lo % BS,
+                      hi - lo, p.v_new + row, stride, D, lane);
+      wrote = true;
     }
     if (wrote) {
       wait_vector_memory();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");     // vector L1 invalidate
     }
     if constexpr (kShared) {
-      if (any_here) {                                      // uniform over the workgroup
-        __syncthreads();
-        if (ablk0 >= 0) { aks0 = sm_ascale[0][0]; avs0 = sm_ascale[0][1]; }
-        if (ablk1 >= 0) { aks1 = sm_ascale[1][0]; avs1 = sm_ascale[1][1]; }
-      }
+      if (any_here) __syncthreads();                       // uniform over the workgroup
     }
   } else {
     const int na = p.append_tail ? Q : (pos >= 0 ? 1 : 0);
@@ -579,8 +557,16 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // past the split end read their block's unused slots, whole groups past it
   // read block 0) and compute masks them.
   const uint32_t lane_off = (uint32_t)lane * 8 * ESZ;
-  auto issue_rows = [&](int j, const char* pool, Vec (&r)[NI], float (&sc)[NI],
-                        const float* scales, bool track, float ov0, float ov1) {
+  // fp8 scales [NB][Hkv] as buffer resources: their loads are vector loads, which
+  // after a fused append read the new scales (see above).
+  // (The host keeps num_blocks * num_kv_heads * 4 below 2^31.)
+  const int scale_bytes = FP8 ? p.num_blocks * p.num_kv_heads * 4 : 0;
+  const auto kscale_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.k_scale, 0, scale_bytes,
+                                                             kBufferRsrcWord3);
+  const auto vscale_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.v_scale, 0, scale_bytes,
+                                                             kBufferRsrcWord3);
+  auto issue_rows = [&](int j, const char* pool, Vec (&r)[NI], float (&sc)[NI], bool is_k,
+                        bool track) {
     const int t0 = chunk_start(j);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -592,10 +578,8 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
             Vec, __builtin_amdgcn_raw_buffer_load_b64(rsrc, lane_off, first * D * ESZ, 0));
         int phys = block_id(j, e);
         phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;
-        float sv = scales[(size_t)phys * p.num_kv_heads + kvh];
-        if (phys == ablk0) sv = ov0;           // a tile this wave just appended to
-        if (phys == ablk1) sv = ov1;
-        sc[i] = sv;
+        sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            is_k ? kscale_rsrc : vscale_rsrc, 0, (phys * p.num_kv_heads + kvh) * 4, 0));
       } else {
         r[i] = __builtin_bit_cast(
             Vec, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, first * D * ESZ, 0));
@@ -713,7 +697,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         *reinterpret_cast<Vec*>(sm_v + (i * TPI + row) * VSTR + 8 * col) = v;
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs_unused, nullptr, false, 0.f, 0.f);
+      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs_unused, false, false);
       __builtin_amdgcn_wave_barrier();
       if (any_need) {
         float al[4];
@@ -754,7 +738,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     // V(j+1) as soon as V(j) is staged in LDS.
     if (my_n > 0) {
       issue_k(0);
-      issue_rows(0, vbase, vr, vs_unused, nullptr, false, 0.f, 0.f);
+      issue_rows(0, vbase, vr, vs_unused, false, false);
     }
     for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
     if (my_n > 0) {
@@ -861,7 +845,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
       if constexpr (NEXT) {
         advance_ids(j);
-        issue_rows(j + 1, kbase, kr, ks, p.k_scale, true, aks0, aks1);
+        issue_rows(j + 1, kbase, kr, ks, true, true);
       }
       __builtin_amdgcn_wave_barrier();
       // this lane's scores: token t = lane / M + q * TSTEP, row sg
@@ -938,15 +922,15 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep V(j+1) behind the value sums of chunk j
-      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs, p.v_scale, false, avs0, avs1);
+      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs, false, false);
     };
 
     // Rotating pipeline: K(j+1) is issued right after the partial scores of chunk
     // j, V(j+1) right after its value sums, so the next chunk's loads fly during
     // compute with no extra registers.
     if (my_n > 0) {
-      issue_rows(0, kbase, kr, ks, p.k_scale, true, aks0, aks1);
-      issue_rows(0, vbase, vr, vs, p.v_scale, false, avs0, avs1);
+      issue_rows(0, kbase, kr, ks, true, true);
+      issue_rows(0, vbase, vr, vs, false, false);
     }
     // Only a wave's last chunk can be partial, so the loop runs the fast path
     // only, and the last chunk is peeled, which also lets every loop iteration

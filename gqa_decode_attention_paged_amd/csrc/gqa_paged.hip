@@ -346,6 +346,9 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   const bool fp8 = s->kv_dtype == GQA_KV_FP8_E4M3;
   if (fp8 && (!k_scale || !v_scale))
     return fail(GQA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
+  if (fp8 && (int64_t)s->num_blocks * s->num_kv_heads * 4 > INT32_MAX)
+    return fail(GQA_ERR_UNSUPPORTED, "fp8 scale arrays of %lld bytes exceed 2 GiB",
+                (long long)s->num_blocks * s->num_kv_heads * 4);
   if (!fp8 && (k_scale || v_scale))
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
   const int G = s->num_q_heads / s->num_kv_heads;
