@@ -23,6 +23,15 @@ For every sequence b and query head h (g = h // G, ctx = context_lens[b]):
 An empty context (ctx = 0) gives out = 0 and lse = -inf (a reading: the pages
 do not treat it).
 
+Scale layouts of fp8 pools (``kv_dtype``):
+* ``"fp8"``: one scale per (block, KV head), k_scale/v_scale [NB][H_kv].
+* ``"fp8_kivi"``: keys scaled per channel and values per token, as KIVI does
+  (*Module 10*, "Quantize the cache": key outliers and value statistics
+  differ; KIVI studies per-channel keys and per-token values; *The Mathematics
+  of Transformer Inference* §11: KV scales per head and per token).  k_scale is
+  [NB][H_kv][d] (one scale per channel of each (block, KV head)), v_scale
+  [NB][H_kv][BS] (one per slot).  value = decode(code) * the element's scale.
+
 Sliding window (``sliding_window = w > 0``): the query, at position ctx - 1,
 attends only to the w most recent tokens, ctx - w .. ctx - 1 (all of them when
 ctx <= w).  *Module 10*, "Parameter count alone does not determine cache size"
@@ -40,8 +49,26 @@ from .fp8 import decode_e4m3fn
 def _widen(pool_rows: np.ndarray, kv_dtype: str) -> np.ndarray:
     if kv_dtype == "bf16":
         return bf16_to_float64(pool_rows)
-    if kv_dtype == "fp8":
+    if kv_dtype in ("fp8", "fp8_kivi"):
         return decode_e4m3fn(pool_rows)
+    raise ValueError(kv_dtype)
+
+
+def dequantized_rows(pool, table_row, ctx, block_size, kv_dtype, scale=None, which="k"):
+    """The first ctx K (``which="k"``) or V rows of one sequence, widened to float64
+    [H_kv][ctx][d] (fp8: decoded and multiplied by each element's scale)."""
+    rows = _widen(gather_sequence(pool, table_row, ctx, block_size), kv_dtype)
+    if kv_dtype == "bf16":
+        return rows
+    t = np.arange(ctx)
+    phys = np.asarray(table_row)[t // block_size]
+    sc = np.asarray(scale, dtype=np.float64)
+    if kv_dtype == "fp8":
+        return rows * sc[phys, :].T[:, :, None]                     # [H_kv][ctx] per token's block
+    if kv_dtype == "fp8_kivi" and which == "k":
+        return rows * np.transpose(sc[phys], (1, 0, 2))              # per channel: [H_kv][ctx][d]
+    if kv_dtype == "fp8_kivi":
+        return rows * sc[phys, :, t % block_size].T[:, :, None]     # per slot (token)
     raise ValueError(kv_dtype)
 
 
@@ -73,7 +100,8 @@ def paged_decode_attention(q_bits, k_pool, v_pool, block_tables, context_lens, b
     q_bits      uint16 [B][H_q][d] (bf16 bit patterns)
     k_pool/v_pool uint16 (bf16) or uint8 (fp8 codes) [NB][H_kv][BS][d]
     block_tables int [B][max_blocks]; context_lens int [B]
-    k_scale/v_scale float32 [NB][H_kv] for fp8 (dequantised value = decode(code) * scale)
+    k_scale/v_scale float32 [NB][H_kv] for fp8 (dequantised value = decode(code) * scale);
+                for fp8_kivi k_scale [NB][H_kv][d] and v_scale [NB][H_kv][BS]
     sliding_window  w > 0 restricts each query to its w most recent tokens (0: all)
     Returns (out float64 [B][H_q][d], lse float64 [B][H_q]).
     """
@@ -86,15 +114,8 @@ def paged_decode_attention(q_bits, k_pool, v_pool, block_tables, context_lens, b
         ctx = int(context_lens[b])
         if ctx == 0:
             continue
-        kr = _widen(gather_sequence(k_pool, block_tables[b], ctx, block_size), kv_dtype)
-        vr = _widen(gather_sequence(v_pool, block_tables[b], ctx, block_size), kv_dtype)
-        if kv_dtype == "fp8":
-            t = np.arange(ctx)
-            phys = np.asarray(block_tables[b])[t // block_size]
-            ks = np.asarray(k_scale, dtype=np.float64)[phys, :].T     # [H_kv][ctx]
-            vs = np.asarray(v_scale, dtype=np.float64)[phys, :].T
-            kr = kr * ks[:, :, None]
-            vr = vr * vs[:, :, None]
+        kr = dequantized_rows(k_pool, block_tables[b], ctx, block_size, kv_dtype, k_scale, "k")
+        vr = dequantized_rows(v_pool, block_tables[b], ctx, block_size, kv_dtype, v_scale, "v")
         lo = max(0, ctx - sliding_window) if sliding_window > 0 else 0
         out[b], lse[b] = dense_decode_attention(q[b], kr[:, lo:], vr[:, lo:], softmax_scale)
     return out, lse

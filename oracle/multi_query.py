@@ -26,9 +26,8 @@ before position ctx - Q + i - w + 1 (see ``oracle.attention``).
 """
 import numpy as np
 
-from .attention import _widen, dense_decode_attention
+from .attention import dense_decode_attention, dequantized_rows
 from .bf16 import bf16_to_float64
-from .cache import gather_sequence
 
 
 def paged_multi_query_attention(q_bits, k_pool, v_pool, block_tables, context_lens, block_size,
@@ -50,13 +49,8 @@ def paged_multi_query_attention(q_bits, k_pool, v_pool, block_tables, context_le
             out[b] = np.nan
             lse[b] = np.nan
             continue
-        kr = _widen(gather_sequence(k_pool, block_tables[b], ctx, block_size), kv_dtype)
-        vr = _widen(gather_sequence(v_pool, block_tables[b], ctx, block_size), kv_dtype)
-        if kv_dtype == "fp8":
-            t = np.arange(ctx)
-            phys = np.asarray(block_tables[b])[t // block_size]
-            kr = kr * np.asarray(k_scale, dtype=np.float64)[phys, :].T[:, :, None]
-            vr = vr * np.asarray(v_scale, dtype=np.float64)[phys, :].T[:, :, None]
+        kr = dequantized_rows(k_pool, block_tables[b], ctx, block_size, kv_dtype, k_scale, "k")
+        vr = dequantized_rows(v_pool, block_tables[b], ctx, block_size, kv_dtype, v_scale, "v")
         for i in range(Q):
             n = ctx - Q + 1 + i                        # tokens up to and including position ctx-Q+i
             lo = max(0, n - sliding_window) if sliding_window > 0 else 0

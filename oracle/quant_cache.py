@@ -34,6 +34,14 @@ with the scale that filling it in one call gives.
 Each division and product is one float32 operation, as the kernel computes it,
 so the codes (integers decided in floating point) match bit for bit.
 
+KIVI layout (``layout="kivi"``, the pool's ``fp8_kivi`` scales, see
+``oracle.attention``): keys keep one scale per channel of each (block, KV
+head) tile and follow the rule above channel by channel (t, the old scale and
+the re-encoding are per channel d, over the column x[:, d] of the new rows);
+values keep one scale per token, p(max|row| / 448) for each new row, set once
+when the row is written.  *Module 10*, "Quantize the cache" (KIVI: per-channel
+keys, per-token values).
+
 Positions of sequence b are start[b] .. start[b] + T - 1 (start < 0: none);
 rows past the block table, or whose table entry is not a block of the pool,
 write nothing.
@@ -79,13 +87,30 @@ def append_tile(tile: np.ndarray, scale: np.float32, first: int, rows32: np.ndar
     return tile, s
 
 
+def _append_tile_kivi(tile, scale, first, rows32, is_key):
+    """KIVI: keys column by column (scale [d]), values row by row (scale [BS])."""
+    tile, scale = tile.copy(), np.array(scale, dtype=np.float32, copy=True)
+    if is_key:
+        for d in range(tile.shape[1]):
+            col, scale[d] = append_tile(tile[:, d:d + 1], scale[d], first, rows32[:, d:d + 1])
+            tile[:, d] = col[:, 0]
+    else:
+        for j in range(rows32.shape[0]):
+            slot = first + j
+            row, scale[slot] = append_tile(tile[slot:slot + 1], scale[slot], 0, rows32[j:j + 1])
+            tile[slot] = row[0]
+    return tile, scale
+
+
 def kv_append_fp8(k_pool, v_pool, k_scale, v_scale, k_new_bits, v_new_bits, block_tables,
-                  start_positions, block_size):
-    """k_pool/v_pool uint8 [NB][H_kv][BS][d]; k_scale/v_scale float32 [NB][H_kv];
+                  start_positions, block_size, layout="block"):
+    """k_pool/v_pool uint8 [NB][H_kv][BS][d]; k_scale/v_scale float32 [NB][H_kv]
+    (layout "kivi": k_scale [NB][H_kv][d], v_scale [NB][H_kv][BS]);
     k_new_bits/v_new_bits uint16 bf16 [B][T][H_kv][d]; start_positions int [B].
     Returns new (k_pool, v_pool, k_scale, v_scale); inputs are not modified."""
     out = []
-    for pool, scale, new in ((k_pool, k_scale, k_new_bits), (v_pool, v_scale, v_new_bits)):
+    for is_key, pool, scale, new in ((True, k_pool, k_scale, k_new_bits),
+                                     (False, v_pool, v_scale, v_new_bits)):
         pool = pool.copy()
         scale = np.array(scale, dtype=np.float32, copy=True)
         x = bf16_to_float64(new).astype(np.float32)          # exact
@@ -104,8 +129,13 @@ def kv_append_fp8(k_pool, v_pool, k_scale, v_scale, k_new_bits, v_new_bits, bloc
                 blk = int(block_tables[b, bi])
                 if 0 <= blk < nb:
                     for h in range(H):
-                        pool[blk, h], scale[blk, h] = append_tile(
-                            pool[blk, h], scale[blk, h], first, x[b, pos - st:pos - st + n, h])
+                        rows = x[b, pos - st:pos - st + n, h]
+                        if layout == "kivi":
+                            pool[blk, h], scale[blk, h] = _append_tile_kivi(
+                                pool[blk, h], scale[blk, h], first, rows, is_key)
+                        else:
+                            pool[blk, h], scale[blk, h] = append_tile(
+                                pool[blk, h], scale[blk, h], first, rows)
                 pos += n
         out += [pool, scale]
     return out[0], out[2], out[1], out[3]

@@ -55,7 +55,7 @@ class Spec:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    kv_dtype: str = "bf16"          # "bf16" or "fp8"
+    kv_dtype: str = "bf16"          # "bf16", "fp8" or "fp8_kivi"
     context: int | tuple = 128       # fixed length, or ("uniform", lo, hi)
     append: bool = False             # last token of each sequence arrives via kv_append
     pool: str = "exact"              # "exact" or "oversized2x"
@@ -211,6 +211,11 @@ def make_case(spec: Spec | str, seed: int = 0, *, context_lens=None,
         vf, vs = _fp8_pool(rng, (num_blocks, Hkv, BS, D), valid)
         out["k_scale"], out["v_scale"] = ks, vs
         nan = FP8_NAN
+    elif spec.kv_dtype == "fp8_kivi":
+        kf, ks = _fp8_pool(rng, (num_blocks, Hkv, BS, D), valid, per="channel")
+        vf, vs = _fp8_pool(rng, (num_blocks, Hkv, BS, D), valid, per="token")
+        out["k_scale"], out["v_scale"] = ks, vs
+        nan = FP8_NAN
     else:
         raise ValueError(spec.kv_dtype)
 
@@ -304,19 +309,24 @@ def new_token_rows(spec: Spec | str, num_tokens: int = 1, seed: int = 0) -> np.n
     return _normal_bf16(rng, (spec.num_seqs, num_tokens, spec.num_kv_heads, spec.head_dim))
 
 
-def _fp8_pool(rng, shape, valid):
-    """N(0,1) float32 source values -> fp8 codes + per-(block, head) scale amax/448."""
+def _fp8_pool(rng, shape, valid, per="block"):
+    """N(0,1) float32 source values -> fp8 codes + scales amax/448 over the valid
+    values of each scale's group: per="block" one per (block, head) [NB][H];
+    "channel" one per (block, head, channel) [NB][H][D]; "token" one per
+    (block, head, slot) [NB][H][BS].  A group with no valid value gets scale 1."""
     NB, H, BS, D = shape
     codes = np.empty(shape, dtype=np.uint8)
-    scales = np.ones((NB, H), dtype=np.float32)
+    axes = {"block": (2, 3), "channel": (2,), "token": (3,)}[per]
+    scales = np.ones({"block": (NB, H), "channel": (NB, H, D), "token": (NB, H, BS)}[per],
+                     dtype=np.float32)
     for b0 in range(0, NB, 256):
         b1 = min(NB, b0 + 256)
         x = _normal_f32(rng, (b1 - b0, H, BS, D))
         m = valid[b0:b1][:, None, :, None]
-        amax = np.max(np.where(m, np.abs(x), 0.0), axis=(2, 3)).astype(np.float32)
+        amax = np.max(np.where(m, np.abs(x), 0.0), axis=axes, keepdims=True).astype(np.float32)
         sc = np.where(amax > 0, amax / np.float32(FP8_E4M3_MAX), np.float32(1.0)).astype(np.float32)
-        scales[b0:b1] = sc
-        codes[b0:b1] = encode_e4m3fn((x / sc[:, :, None, None]).astype(np.float32))
+        scales[b0:b1] = sc.reshape(scales[b0:b1].shape)
+        codes[b0:b1] = encode_e4m3fn((x / sc).astype(np.float32))
     return codes, scales
 
 
