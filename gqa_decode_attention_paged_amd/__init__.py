@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_page
 
 GQA_KV_BF16 = 0
 GQA_KV_FP8_E4M3 = 1
+GQA_KV_FP8_E4M3_KIVI = 2
 GQA_FLAG_BATCH_INVARIANT = 1
 STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
                 3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
@@ -127,9 +128,11 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _kv_dtype(cache) -> int:
+def _kv_dtype(cache, k_scale=None) -> int:
     import torch
     if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        if k_scale is not None and k_scale.dim() == 3:
+            return GQA_KV_FP8_E4M3_KIVI
         return GQA_KV_FP8_E4M3
     if cache.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return GQA_KV_BF16
@@ -137,11 +140,13 @@ def _kv_dtype(cache) -> int:
 
 
 def make_shape(num_seqs, num_q_heads, k_cache, block_tables, batch_invariant=False,
-               sliding_window=0) -> PagedShape:
+               sliding_window=0, k_scale=None) -> PagedShape:
+    """The shape of a call.  An fp8 pool whose k_scale is [NB][H_kv][d_h] (one scale
+    per channel) has the KIVI layout."""
     nb, hkv, bs, d = k_cache.shape
     return PagedShape(num_seqs, num_q_heads, hkv, d, bs, nb, block_tables.shape[1],
-                      _kv_dtype(k_cache), GQA_FLAG_BATCH_INVARIANT if batch_invariant else 0,
-                      int(sliding_window))
+                      _kv_dtype(k_cache, k_scale),
+                      GQA_FLAG_BATCH_INVARIANT if batch_invariant else 0, int(sliding_window))
 
 
 def num_splits(context_len: int) -> int:
@@ -186,7 +191,7 @@ def paged_decode_multi_query(q, k_cache, v_cache, block_tables, context_lens, ma
     import torch
     lib = load()
     B, Q, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -211,7 +216,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
     import torch
     lib = load()
     B, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -239,7 +244,7 @@ def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tab
     import torch
     lib = load()
     B, Q, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -275,7 +280,7 @@ def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, 
     import torch
     lib = load()
     B, Hq, D = q.shape
-    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window)
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -302,14 +307,15 @@ def workspace_init(shape: PagedShape, max_context_len: int, workspace):
 
 def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
                   start_positions):
-    """Quantise and write new tokens into an fp8 pool with per-(block, KV head)
-    scales: k_new/v_new bf16 [B][H_kv][d_h] (one token) or [B][T][H_kv][d_h] at
-    positions start_positions[b] + j (in place, scales included)."""
+    """Quantise and write new tokens into an fp8 pool: k_new/v_new bf16 [B][H_kv][d_h]
+    (one token) or [B][T][H_kv][d_h] at positions start_positions[b] + j (in place,
+    scales included).  Scales [NB][H_kv] (per (block, head)) or the KIVI layout
+    (k_scale [NB][H_kv][d_h], v_scale [NB][H_kv][BS])."""
     lib = load()
     if k_new.dim() == 3:
         k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
     B, T = k_new.shape[0], k_new.shape[1]
-    shape = make_shape(B, k_cache.shape[1], k_cache, block_tables)
+    shape = make_shape(B, k_cache.shape[1], k_cache, block_tables, k_scale=k_scale)
     _check(lib.gqa_kv_append_fp8(ctypes.byref(shape), int(T), _ptr(k_new), _ptr(v_new),
                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(block_tables), _ptr(start_positions), _stream(k_cache)))
@@ -319,7 +325,7 @@ def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_sca
     """Copy-on-write block copy: block dst_blocks[j] of both pools (and the fp8 scales)
     becomes a copy of src_blocks[j], in place."""
     nb, hkv, bs, d = k_cache.shape
-    shape = PagedShape(1, hkv, hkv, d, bs, nb, 1, _kv_dtype(k_cache), 0, 0)
+    shape = PagedShape(1, hkv, hkv, d, bs, nb, 1, _kv_dtype(k_cache, k_scale), 0, 0)
     _check(load().gqa_kv_copy_blocks(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(k_scale), _ptr(v_scale), _ptr(src_blocks),
                                      _ptr(dst_blocks), int(src_blocks.numel()),

@@ -251,10 +251,15 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
 }
 
-template <int D, int BS, int M, bool FP8, int WAVES>
+// KV: 0 bf16 pools; 1 fp8 pools with one scale per (block, KV head); 2 fp8 pools
+// with the KIVI layout (keys scaled per channel of each (block, KV head), values
+// per token).
+template <int D, int BS, int M, int KV, int WAVES>
 // Launch bounds ask for two resident waves per SIMD (one 8-wave or two 4-wave
 // workgroups per CU), which caps registers at 256 per lane.
 __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(DecodeParams p) {
+  constexpr bool FP8 = KV != 0;
+  constexpr bool KIVI = KV == 2;
   // M is the row capacity: the rows of one (sequence, KV head) are its query
   // positions times its G query heads, row m = i*G + g (R = G*Q <= M of them).
   // bf16 pools with two or more rows use the matrix path; fp8 pools and single
@@ -421,7 +426,9 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   const bool pos_in_split = !degenerate && pos >= base && pos < ctx;
   const int owner = pos_in_split ? (pos - base) / plan.split_tokens : 0;
   if (p.positions && split == owner && !pos_in_split) {
-    if constexpr (FP8) {
+    if constexpr (KIVI) {
+      // the host rejects a fused append into a KIVI pool
+    } else if constexpr (FP8) {
       if (wave == 0 && pos >= 0 && pos < p.max_blocks * BS) {
         const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / BS];
         if ((unsigned)blk < (unsigned)p.num_blocks) {
@@ -462,7 +469,9 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // vector load of the tile or of its scale (buffer loads, both) reads them
   // from L2.  When a block spans several chunks (BS > CT) other waves read it
   // too, and the workgroup waits for the append before any tile is read.
-  if constexpr (FP8) {
+  if constexpr (KIVI) {
+    // the host rejects a fused append into a KIVI pool
+  } else if constexpr (FP8) {
     constexpr bool kShared = BS > CT;
     const int na = p.append_tail ? Q : (pos >= 0 ? 1 : 0);
     const int a0 = p.append_tail ? ctx - Q : pos;
@@ -559,12 +568,20 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   const uint32_t lane_off = (uint32_t)lane * 8 * ESZ;
   // fp8 scales [NB][Hkv] as buffer resources: their loads are vector loads, which
   // after a fused append read the new scales (see above).
-  // (The host keeps num_blocks * num_kv_heads * 4 below 2^31.)
-  const int scale_bytes = FP8 ? p.num_blocks * p.num_kv_heads * 4 : 0;
-  const auto kscale_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.k_scale, 0, scale_bytes,
+  // KIVI: k_scale [NB][Hkv][D], v_scale [NB][Hkv][BS].  (The host keeps these
+  // byte counts below 2^31.)
+  constexpr int KSPB = KIVI ? D : 1;                  // k scales per (block, KV head)
+  constexpr int VSPB = KIVI ? BS : 1;                 // v scales per (block, KV head)
+  const int kscale_bytes = FP8 ? p.num_blocks * p.num_kv_heads * KSPB * 4 : 0;
+  const int vscale_bytes = FP8 ? p.num_blocks * p.num_kv_heads * VSPB * 4 : 0;
+  const auto kscale_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.k_scale, 0, kscale_bytes,
                                                              kBufferRsrcWord3);
-  const auto vscale_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.v_scale, 0, scale_bytes,
+  const auto vscale_rsrc = __builtin_amdgcn_make_buffer_rsrc(p.v_scale, 0, vscale_bytes,
                                                              kBufferRsrcWord3);
+  // KIVI keys: this lane's 8 channel scales for each block of a chunk, loaded
+  // with the chunk's K rows.
+  constexpr int KCB = KIVI ? (CT >= BS ? CT / BS : 1) : 1;
+  float kcs[KCB][8];
   auto issue_rows = [&](int j, const char* pool, Vec (&r)[NI], float (&sc)[NI], bool is_k,
                         bool track) {
     const int t0 = chunk_start(j);
@@ -578,8 +595,31 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
             Vec, __builtin_amdgcn_raw_buffer_load_b64(rsrc, lane_off, first * D * ESZ, 0));
         int phys = block_id(j, e);
         phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;
-        sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            is_k ? kscale_rsrc : vscale_rsrc, 0, (phys * p.num_kv_heads + kvh) * 4, 0));
+        if constexpr (KIVI) {
+          if (is_k) {
+            // the block's channel scales for this lane's 8 dims, once per block
+            if (CT >= BS ? (i * TPI) % BS == 0 : i == 0) {
+              const int off = ((phys * p.num_kv_heads + kvh) * D + col * 8) * 4;
+              const f32x4 a = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(kscale_rsrc, 0, off, 0));
+              const f32x4 b = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(kscale_rsrc, 0, off + 16, 0));
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                kcs[e][k] = a[k];
+                kcs[e][4 + k] = b[k];
+              }
+            }
+          } else {
+            // the value scale of this lane's token (its slot in the block)
+            const int slot = (t0 + i * TPI + row) % BS;
+            sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                vscale_rsrc, 0, ((phys * p.num_kv_heads + kvh) * BS + slot) * 4, 0));
+          }
+        } else {
+          sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+              is_k ? kscale_rsrc : vscale_rsrc, 0, (phys * p.num_kv_heads + kvh) * 4, 0));
+        }
       } else {
         r[i] = __builtin_bit_cast(
             Vec, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, first * D * ESZ, 0));
@@ -812,14 +852,30 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         // zero V rows past the split end (their slots may hold NaN poison)
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-          if (i * TPI + row >= nvalid) vr[i] = Vec{};
+          if (i * TPI + row >= nvalid) {
+            vr[i] = Vec{};
+            if constexpr (KIVI) vs[i] = 0.f;           // a slot past the end: any scale
+          }
       }
       // partial dot products of this lane's 8 dims, per head
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const Vec kk = kr[i];
         float part[M];
-        if constexpr (FP8) {
+        if constexpr (KIVI) {
+          float kf[8];
+          widen8<true>(kk, kf);
+          const int e = CT >= BS ? (i * TPI) / BS : 0;      // constant once unrolled
+#pragma unroll
+          for (int k = 0; k < 8; ++k) kf[k] *= kcs[e][k];
+#pragma unroll
+          for (int g = 0; g < M; ++g) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a = fmaf(qf[g][k], kf[k], a);
+            part[g] = a;
+          }
+        } else if constexpr (FP8) {
           float kf[8];
           widen8<true>(kk, kf);
 #pragma unroll

@@ -61,7 +61,8 @@ gqa_status check_shape(const gqa_paged_shape* s) {
     return fail(GQA_ERR_UNSUPPORTED, "head_dim=%d not in {64,128}", s->head_dim);
   if (s->block_size != 16 && s->block_size != 32)
     return fail(GQA_ERR_UNSUPPORTED, "block_size=%d not in {16,32}", s->block_size);
-  if (s->kv_dtype != GQA_KV_BF16 && s->kv_dtype != GQA_KV_FP8_E4M3)
+  if (s->kv_dtype != GQA_KV_BF16 && s->kv_dtype != GQA_KV_FP8_E4M3 &&
+      s->kv_dtype != GQA_KV_FP8_E4M3_KIVI)
     return fail(GQA_ERR_UNSUPPORTED, "kv_dtype=%d unknown", s->kv_dtype);
   if (s->flags & ~GQA_FLAG_BATCH_INVARIANT)
     return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)s->flags);
@@ -127,19 +128,23 @@ int64_t max_span(const gqa_paged_shape* s, int32_t max_context_len, int32_t num_
 constexpr int kMaxRowsBf16 = 16;
 constexpr int kMaxRowsFp8 = 8;
 
+// kv: 0 bf16, 1 fp8 with (block, KV head) scales, 2 fp8 with the KIVI layout.
 template <int D, int BS, int M, int W>
-const void* pick_kernel_m(bool fp8) {
+const void* pick_kernel_m(int kv) {
   if constexpr (M > kMaxRowsFp8) {
-    return fp8 ? nullptr
-               : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, false, W>);
+    return kv ? nullptr : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 0, W>);
   } else {
-    return fp8 ? reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, true, W>)
-               : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, false, W>);
+    switch (kv) {
+      case 0: return reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 0, W>);
+      case 1: return reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 1, W>);
+      case 2: return reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 2, W>);
+    }
+    return nullptr;
   }
 }
 
 template <int D, int BS, int W>
-const void* pick_kernel_bs(int M, bool fp8) {
+const void* pick_kernel_bs(int M, int fp8) {
   switch (M) {
     case 1: return pick_kernel_m<D, BS, 1, W>(fp8);
     case 2: return pick_kernel_m<D, BS, 2, W>(fp8);
@@ -151,13 +156,13 @@ const void* pick_kernel_bs(int M, bool fp8) {
 }
 
 template <int W>
-const void* pick_kernel_w(int D, int BS, int M, bool fp8) {
+const void* pick_kernel_w(int D, int BS, int M, int fp8) {
   if (D == 64)
     return BS == 16 ? pick_kernel_bs<64, 16, W>(M, fp8) : pick_kernel_bs<64, 32, W>(M, fp8);
   return BS == 16 ? pick_kernel_bs<128, 16, W>(M, fp8) : pick_kernel_bs<128, 32, W>(M, fp8);
 }
 
-const void* pick_kernel(int D, int BS, int M, bool fp8, int waves) {
+const void* pick_kernel(int D, int BS, int M, int fp8, int waves) {
   return waves == 8 ? pick_kernel_w<8>(D, BS, M, fp8) : pick_kernel_w<4>(D, BS, M, fp8);
 }
 
@@ -296,8 +301,9 @@ gqa_status gqa_kv_append_fp8(const gqa_paged_shape* s, int32_t num_tokens, const
   if (st != GQA_OK) return st;
   if (num_tokens < 0 || num_tokens > 65535)
     return fail(GQA_ERR_INVALID_ARG, "num_tokens %d outside [0, 65535]", num_tokens);
-  if (s->kv_dtype != GQA_KV_FP8_E4M3)
+  if (s->kv_dtype == GQA_KV_BF16)
     return fail(GQA_ERR_INVALID_ARG, "kv_append_fp8 needs an fp8 pool (use kv_append for bf16)");
+  const bool kivi = s->kv_dtype == GQA_KV_FP8_E4M3_KIVI;
   if (s->num_seqs == 0 || num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
       !start_positions)
@@ -321,7 +327,8 @@ gqa_status gqa_kv_append_fp8(const gqa_paged_shape* s, int32_t num_tokens, const
   p.block_size = s->block_size;
   p.num_blocks = s->num_blocks;
   p.max_blocks = s->max_blocks_per_seq;
-  st = launch(reinterpret_cast<const void*>(&gqa::kv_append_fp8_kernel),
+  st = launch(kivi ? reinterpret_cast<const void*>(&gqa::kv_append_fp8_kivi_kernel)
+                   : reinterpret_cast<const void*>(&gqa::kv_append_fp8_kernel),
               dim3(s->num_seqs, s->num_kv_heads, 2), dim3(256), &p, "kv_append_fp8", stream);
   return st == GQA_OK ? ok() : st;
 }
@@ -343,12 +350,17 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
                 max_context_len);
   if (!std::isfinite(softmax_scale))
     return fail(GQA_ERR_INVALID_ARG, "softmax_scale is not finite");
-  const bool fp8 = s->kv_dtype == GQA_KV_FP8_E4M3;
+  const bool fp8 = s->kv_dtype != GQA_KV_BF16;
+  const bool kivi = s->kv_dtype == GQA_KV_FP8_E4M3_KIVI;
   if (fp8 && (!k_scale || !v_scale))
     return fail(GQA_ERR_INVALID_ARG, "fp8 pools need k_scale and v_scale");
-  if (fp8 && (int64_t)s->num_blocks * s->num_kv_heads * 4 > INT32_MAX)
+  const int64_t scales_per_tile = kivi ? (s->head_dim > s->block_size ? s->head_dim : s->block_size) : 1;
+  if (fp8 && (int64_t)s->num_blocks * s->num_kv_heads * scales_per_tile * 4 > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "fp8 scale arrays of %lld bytes exceed 2 GiB",
-                (long long)s->num_blocks * s->num_kv_heads * 4);
+                (long long)s->num_blocks * s->num_kv_heads * scales_per_tile * 4);
+  if (kivi && (positions || append_tail))
+    return fail(GQA_ERR_UNSUPPORTED, "the fused append takes bf16 and per-(block, head) fp8 "
+                "pools; append to a KIVI pool with gqa_kv_append_fp8");
   if (!fp8 && (k_scale || v_scale))
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
   const int G = s->num_q_heads / s->num_kv_heads;
@@ -376,7 +388,8 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   if (!aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const int waves = pick_waves(s);
-  const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows), fp8, waves);
+  const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows),
+                               kivi ? 2 : fp8 ? 1 : 0, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
   const int target = target_splits(s, fn, waves * 64);
   const int launch_splits = split_bound(max_span(s, max_context_len, num_queries), target);
@@ -509,7 +522,8 @@ gqa_status gqa_kv_copy_blocks(const gqa_paged_shape* s, void* k_cache, void* v_c
   if (st != GQA_OK) return st;
   if (num_pairs < 0 || num_pairs > INT32_MAX / 2)
     return fail(GQA_ERR_INVALID_ARG, "num_pairs %d out of range", num_pairs);
-  const bool fp8 = s->kv_dtype == GQA_KV_FP8_E4M3;
+  const bool fp8 = s->kv_dtype != GQA_KV_BF16;
+  const bool kivi = s->kv_dtype == GQA_KV_FP8_E4M3_KIVI;
   if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr))
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale are required for fp8 pools and must be "
                 "NULL for bf16");
@@ -526,7 +540,8 @@ gqa_status gqa_kv_copy_blocks(const gqa_paged_shape* s, void* k_cache, void* v_c
   p.src = src_blocks;
   p.dst = dst_blocks;
   p.num_blocks = s->num_blocks;
-  p.num_kv_heads = s->num_kv_heads;
+  p.k_scales = s->num_kv_heads * (kivi ? s->head_dim : 1);
+  p.v_scales = s->num_kv_heads * (kivi ? s->block_size : 1);
   p.block_bytes = (int64_t)s->num_kv_heads * s->block_size * s->head_dim * (fp8 ? 1 : 2);
   const int64_t slices = (p.block_bytes + gqa::kCopySliceBytes - 1) / gqa::kCopySliceBytes;
   if (slices > 65535)
@@ -558,7 +573,7 @@ gqa_status gqa_kv_gather(const gqa_paged_shape* s, const void* cache, const int3
   p.block_size = s->block_size;
   p.num_blocks = s->num_blocks;
   p.num_tokens = num_tokens;
-  p.row_bytes = s->head_dim * (s->kv_dtype == GQA_KV_FP8_E4M3 ? 1 : 2);
+  p.row_bytes = s->head_dim * (s->kv_dtype != GQA_KV_BF16 ? 1 : 2);
   st = launch(reinterpret_cast<const void*>(&gqa::kv_gather_kernel),
               dim3((num_tokens + 63) / 64, s->num_kv_heads), dim3(256), &p, "kv_gather", stream);
   return st == GQA_OK ? ok() : st;

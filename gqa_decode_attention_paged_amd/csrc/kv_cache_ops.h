@@ -156,6 +156,78 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendFp8Params p) {
   }
 }
 
+// KIVI layout (k_scale [NB][Hkv][D], v_scale [NB][Hkv][BS]).  grid (B, Hkv, 2),
+// 256 threads.  Keys (z = 0): thread d owns channel d of each tile its new rows
+// fall in and applies the rule of kv_append_fp8_kernel to that column (t = its
+// amax / 448, growth and re-encoding per channel).  Values (z = 1): each wave
+// takes whole new rows; a row's scale is pow2_ceil(amax(row) / 448), set once.
+__global__ __launch_bounds__(256) void kv_append_fp8_kivi_kernel(AppendFp8Params p) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int st = p.start[b];
+  if (st < 0) return;
+  const int BS = p.block_size, D = p.head_dim;
+  const int64_t end = (int64_t)st + p.num_tokens;
+  const size_t row_stride = (size_t)p.num_kv_heads * D;        // between tokens of k_new
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t pos = st; pos < end;) {
+    const int64_t bi = pos / BS;
+    const int first = (int)(pos % BS);
+    const int n = (int)(end - pos < BS - first ? end - pos : BS - first);
+    if (bi >= p.max_blocks) break;
+    const int blk = p.block_tables[(size_t)b * p.max_blocks + bi];
+    if ((unsigned)blk < (unsigned)p.num_blocks) {
+      const size_t tile_off = ((size_t)blk * p.num_kv_heads + h) * BS * D;
+      const size_t row0 = (((size_t)b * p.num_tokens + (size_t)(pos - st)) * p.num_kv_heads + h) * D;
+      if (!is_v) {
+        uint8_t* tile = p.k_cache + tile_off;
+        const uint16_t* rows = p.k_new + row0;
+        for (int d = threadIdx.x; d < D; d += 256) {
+          float am = 0.f;
+          for (int j = 0; j < n; ++j)
+            am = __builtin_fmaxf(am, __builtin_fabsf(__uint_as_float((uint32_t)rows[j * row_stride + d] << 16)));
+          float* sp = p.k_scale + ((size_t)blk * p.num_kv_heads + h) * D + d;
+          const float old = *sp;
+          const float t = am / kFp8Max;
+          const float s = (first > 0 && old >= t) ? old : pow2_ceil(t);
+          if (first > 0 && t > old) {
+            for (int j = 0; j < first; ++j) {
+              const uint8_t c = tile[(size_t)j * D + d];
+              const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c), false);
+              const float v[4] = {f[0] * old, 0.f, 0.f, 0.f};
+              tile[(size_t)j * D + d] = (uint8_t)(encode4_e4m3(v, s) & 0xff);
+            }
+          }
+          for (int j = 0; j < n; ++j) {
+            const float v[4] = {__uint_as_float((uint32_t)rows[j * row_stride + d] << 16), 0.f, 0.f, 0.f};
+            tile[(size_t)(first + j) * D + d] = (uint8_t)(encode4_e4m3(v, s) & 0xff);
+          }
+          *sp = s;
+        }
+      } else {
+        uint8_t* tile = p.v_cache + tile_off;
+        const uint16_t* rows = p.v_new + row0;
+        for (int j = wave; j < n; j += 4) {                  // one wave per new row
+          float am = 0.f;
+          for (int d = lane; d < D; d += 64)
+            am = __builtin_fmaxf(am, __builtin_fabsf(__uint_as_float((uint32_t)rows[j * row_stride + d] << 16)));
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) am = __builtin_fmaxf(am, __shfl_xor(am, o));
+          const float s = pow2_ceil(am / kFp8Max);
+          for (int q = lane; q < D / 4; q += 64) {
+            const uint2 w = *reinterpret_cast<const uint2*>(rows + j * row_stride + q * 4);
+            const float v[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+            reinterpret_cast<uint32_t*>(tile + (size_t)(first + j) * D)[q] = encode4_e4m3(v, s);
+          }
+          if (lane == 0) p.v_scale[((size_t)blk * p.num_kv_heads + h) * BS + first + j] = s;
+        }
+      }
+    }
+    pos += n;
+  }
+}
+
 constexpr int kCopyThreads = 256;
 constexpr int kCopySliceBytes = kCopyThreads * 16;       // 4 KiB of each pool per workgroup
 
@@ -167,7 +239,8 @@ struct CopyBlocksParams {
   const int32_t* src;           // [num_pairs] source block ids
   const int32_t* dst;           // [num_pairs] destination block ids
   int32_t num_blocks;
-  int32_t num_kv_heads;
+  int32_t k_scales;             // fp8 scales per block: Hkv (per (block, head)), Hkv * D (KIVI keys)
+  int32_t v_scales;             //   Hkv, or Hkv * BS (KIVI values)
   int64_t block_bytes;          // Hkv * BS * row_bytes, a multiple of 16
 };
 
@@ -192,10 +265,10 @@ __global__ __launch_bounds__(kCopyThreads) void kv_copy_blocks_kernel(CopyBlocks
     *reinterpret_cast<uint4*>(p.v_cache + (size_t)dst * p.block_bytes + off) = vv;
   }
   if (p.k_scale && blockIdx.y == 0) {
-    for (int h = threadIdx.x; h < p.num_kv_heads; h += kCopyThreads) {
-      p.k_scale[(size_t)dst * p.num_kv_heads + h] = p.k_scale[(size_t)src * p.num_kv_heads + h];
-      p.v_scale[(size_t)dst * p.num_kv_heads + h] = p.v_scale[(size_t)src * p.num_kv_heads + h];
-    }
+    for (int h = threadIdx.x; h < p.k_scales; h += kCopyThreads)
+      p.k_scale[(size_t)dst * p.k_scales + h] = p.k_scale[(size_t)src * p.k_scales + h];
+    for (int h = threadIdx.x; h < p.v_scales; h += kCopyThreads)
+      p.v_scale[(size_t)dst * p.v_scales + h] = p.v_scale[(size_t)src * p.v_scales + h];
   }
 }
 

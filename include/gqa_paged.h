@@ -79,9 +79,18 @@ typedef enum gqa_status {
   GQA_ERR_HIP = 4            /* a HIP launch failed; see gqa_last_error()         */
 } gqa_status;
 
+/* Stored K/V element type and, for fp8, the layout of the fp32 scales
+ * (value = decode(code) * scale):
+ *   GQA_KV_FP8_E4M3       k_scale, v_scale [num_blocks][H_kv]: one per (block, KV head)
+ *   GQA_KV_FP8_E4M3_KIVI  k_scale [num_blocks][H_kv][head_dim]: one per channel of each
+ *                         (block, KV head); v_scale [num_blocks][H_kv][block_size]: one
+ *                         per token (slot) -- keys per channel and values per token, as
+ *                         KIVI quantises them (*Module 10*, "Quantize the cache"; *The
+ *                         Mathematics of Transformer Inference* §11). */
 typedef enum gqa_kv_dtype {
   GQA_KV_BF16 = 0,
-  GQA_KV_FP8_E4M3 = 1
+  GQA_KV_FP8_E4M3 = 1,
+  GQA_KV_FP8_E4M3_KIVI = 2
 } gqa_kv_dtype;
 
 /* Shape flags. */

@@ -205,3 +205,14 @@ def test_append_fp8_validation(lib):
     assert ap(ctypes.byref(f), 0, *args, None) == 0                   # nothing to write
     assert ap(ctypes.byref(f), 1, *([P(16)] * 4), None, P(16), P(16), P(16), None) == 1
     assert ap(ctypes.byref(f), 1, P(8), *([P(16)] * 7), None) == 1      # misaligned rows
+
+
+def test_kivi_dtype_is_accepted_and_fused_append_refused(lib):
+    P = ctypes.c_void_p
+    k = _shape(kv_dtype=2)
+    assert lib.gqa_paged_decode_workspace_size(ctypes.byref(k), 1000) > 0
+    call = lambda shape: lib.gqa_paged_decode_append_attention(
+        ctypes.byref(shape), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16),
+        P(16), 100, 0.1, P(16), None, P(16), 1 << 30, None)
+    assert call(k) == 2
+    assert lib.gqa_paged_decode_workspace_size(ctypes.byref(_shape(kv_dtype=3)), 1000) == 0

@@ -75,6 +75,8 @@ SPECS = {
                  pool="oversized2x"),
     "mha_fp8": Spec("mha_fp8", 4, 4, 40, 40, 128, 16, kv_dtype="fp8", context=8192,
                     pool="exact"),
+    "mha_fp8_kivi": Spec("mha_fp8_kivi", 5, 4, 40, 40, 128, 16, kv_dtype="fp8_kivi",
+                         context=8192, pool="exact"),
 }
 
 
