@@ -20,6 +20,10 @@ Workload ``mha_fp8_append`` is the fp8 decode step on the 40-head MHA shape:
 the quantising append of each sequence's new token (power-of-two scale per
 (block, KV head), grown if needed) fused with fp8 attention, one launch.
 
+Workload ``mha_fp8_kivi`` is the 40-head MHA shape with the KIVI scale layout
+(keys scaled per channel of each block, values per token); its bytes include
+those scales.
+
 Workload ``cow_fork`` measures the copy-on-write block copy instead: 256 prompts
 on the 8K grouped-query pool geometry each fork into 8 parallel samples, so each
 prompt's partially filled last block is copied to 7 fresh blocks (1792 copies,
@@ -49,14 +53,18 @@ METRIC = "decode-attention KV-read HBM GB/s (% of MI355X peak) and µs/step"
 
 
 def kv_bytes_per_step(spec, context_lens):
-    """Algorithmic bytes: every attended K and V element at stored width, plus fp8 scales."""
+    """Algorithmic bytes: every attended K and V element at stored width, plus the fp8
+    scales of the attended blocks (one K and one V scale per (block, KV head); KIVI:
+    d_h key scales and block_size value scales)."""
     import numpy as np
-    esz = 1 if spec.kv_dtype == "fp8" else 2
+    esz = 1 if spec.kv_dtype.startswith("fp8") else 2
     ctx = context_lens.astype(np.int64)
     total = int(ctx.sum()) * spec.num_kv_heads * spec.head_dim * 2 * esz
+    nb = (ctx + spec.block_size - 1) // spec.block_size
     if spec.kv_dtype == "fp8":
-        nb = (ctx + spec.block_size - 1) // spec.block_size
         total += int(nb.sum()) * spec.num_kv_heads * 2 * 4
+    elif spec.kv_dtype == "fp8_kivi":
+        total += int(nb.sum()) * spec.num_kv_heads * (spec.head_dim + spec.block_size) * 4
     return total
 
 
@@ -201,7 +209,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b",
                     choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4",
-                             "mha_fp8_append", "cow_fork"])
+                             "mha_fp8_append", "mha_fp8_kivi", "cow_fork"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -323,6 +331,9 @@ def main():
                   "attention + log-sum-exp merge)")
     elif k_new is not None:
         kernel = "paged_decode_kernel (fused KV append + split attention + log-sum-exp merge)"
+    elif spec.kv_dtype == "fp8_kivi":
+        kernel = ("paged_decode_kernel (fp8 with KIVI scales: per-channel keys, per-token "
+                  "values; split attention + log-sum-exp merge)")
     else:
         kernel = "paged_decode_kernel (split attention + log-sum-exp merge)"
 
@@ -339,6 +350,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if spec.kv_dtype == "bf16" else "fp8",
+        # fp8 stores E4M3 codes; the arithmetic is fp32 after dequantisation
         "data": "synthetic (seeded N(0,1) q/k/v, random block placement; no weights)",
         "config": {
             "workload": args.workload, "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,

@@ -598,12 +598,13 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         if constexpr (KIVI) {
           if (is_k) {
             // the block's channel scales for this lane's 8 dims, once per block
+            // (per-lane part in voffset, the block's part in the uniform soffset)
             if (CT >= BS ? (i * TPI) % BS == 0 : i == 0) {
-              const int off = ((phys * p.num_kv_heads + kvh) * D + col * 8) * 4;
+              const int tile = (phys * p.num_kv_heads + kvh) * D * 4;
               const f32x4 a = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(kscale_rsrc, 0, off, 0));
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(kscale_rsrc, col * 32, tile, 0));
               const f32x4 b = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(kscale_rsrc, 0, off + 16, 0));
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(kscale_rsrc, col * 32 + 16, tile, 0));
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 kcs[e][k] = a[k];
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
             // the value scale of this lane's token (its slot in the block)
             const int slot = (t0 + i * TPI + row) % BS;
             sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                vscale_rsrc, 0, ((phys * p.num_kv_heads + kvh) * BS + slot) * 4, 0));
+                vscale_rsrc, slot * 4, (phys * p.num_kv_heads + kvh) * BS * 4, 0));
           }
         } else {
           sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
