@@ -425,21 +425,26 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
   const bool pos_in_split = !degenerate && pos >= base && pos < ctx;
   const int owner = pos_in_split ? (pos - base) / plan.split_tokens : 0;
-  if (p.positions && split == owner && !pos_in_split) {
+  // One wave quantises new rows into one fp8 (block, KV head) tile, either layout.
+  auto append_fp8_tile = [&](int blk, int first, int n, size_t row, size_t stride) {
+    const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * BS * D;
+    const size_t sidx = (size_t)blk * p.num_kv_heads + kvh;
+    uint8_t* kt = static_cast<uint8_t*>(p.k_cache) + tile;
+    uint8_t* vt = static_cast<uint8_t*>(p.v_cache) + tile;
     if constexpr (KIVI) {
-      // the host rejects a fused append into a KIVI pool
-    } else if constexpr (FP8) {
+      wave_append_fp8_kivi(kt, vt, p.k_scale + sidx * D, p.v_scale + sidx * BS, first, n,
+                           p.k_new + row, p.v_new + row, stride, D, lane);
+    } else {
+      wave_append_fp8(kt, p.k_scale + sidx, first, n, p.k_new + row, stride, D, lane);
+      wave_append_fp8(vt, p.v_scale + sidx, first, n, p.v_new + row, stride, D, lane);
+    }
+  };
+  if (p.positions && split == owner && !pos_in_split) {
+    if constexpr (FP8) {
       if (wave == 0 && pos >= 0 && pos < p.max_blocks * BS) {
         const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks) {
-          const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * BS * D;
-          const size_t row = ((size_t)b * p.num_kv_heads + kvh) * D;
-          const size_t sidx = (size_t)blk * p.num_kv_heads + kvh;
-          wave_append_fp8(static_cast<uint8_t*>(p.k_cache) + tile, p.k_scale + sidx, pos % BS, 1,
-                          p.k_new + row, 0, D, lane);
-          wave_append_fp8(static_cast<uint8_t*>(p.v_cache) + tile, p.v_scale + sidx, pos % BS, 1,
-                          p.v_new + row, 0, D, lane);
-        }
+        if ((unsigned)blk < (unsigned)p.num_blocks)
+          append_fp8_tile(blk, pos % BS, 1, ((size_t)b * p.num_kv_heads + kvh) * D, 0);
       }
     } else {
       append_rows(p, b, kvh, pos, D, BS);
@@ -469,9 +474,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // vector load of the tile or of its scale (buffer loads, both) reads them
   // from L2.  When a block spans several chunks (BS > CT) other waves read it
   // too, and the workgroup waits for the append before any tile is read.
-  if constexpr (KIVI) {
-    // the host rejects a fused append into a KIVI pool
-  } else if constexpr (FP8) {
+  if constexpr (FP8) {
     constexpr bool kShared = BS > CT;
     const int na = p.append_tail ? Q : (pos >= 0 ? 1 : 0);
     const int a0 = p.append_tail ? ctx - Q : pos;
@@ -488,13 +491,8 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
       any_here = true;
       if (((lo - s0) / CT) % WAVES != wave) continue;
-      const size_t tile = ((size_t)blk * p.num_kv_heads + kvh) * BS * D;
       const size_t row = (((size_t)b * rows_per_seq + (lo - a0)) * p.num_kv_heads + kvh) * D;
-      const size_t sidx = (size_t)blk * p.num_kv_heads + kvh;
-      wave_append_fp8(static_cast<uint8_t*>(p.k_cache) + tile, p.k_scale + sidx, lo % BS,
-                      hi - lo, p.k_new + row, stride, D, lane);
-      wave_append_fp8(static_cast<uint8_t*>(p.v_cache) + tile, p.v_scale + sidx, lo % BS,
-                      hi - lo, p.v_new + row, stride, D, lane);
+      append_fp8_tile(blk, lo % BS, hi - lo, row, stride);
       wrote = true;
     }
     if (wrote) {

@@ -358,9 +358,6 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   if (fp8 && (int64_t)s->num_blocks * s->num_kv_heads * scales_per_tile * 4 > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "fp8 scale arrays of %lld bytes exceed 2 GiB",
                 (long long)s->num_blocks * s->num_kv_heads * scales_per_tile * 4);
-  if (kivi && (positions || append_tail))
-    return fail(GQA_ERR_UNSUPPORTED, "the fused append takes bf16 and per-(block, head) fp8 "
-                "pools; append to a KIVI pool with gqa_kv_append_fp8");
   if (!fp8 && (k_scale || v_scale))
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
   const int G = s->num_q_heads / s->num_kv_heads;

@@ -207,12 +207,14 @@ def test_append_fp8_validation(lib):
     assert ap(ctypes.byref(f), 1, P(8), *([P(16)] * 7), None) == 1      # misaligned rows
 
 
-def test_kivi_dtype_is_accepted_and_fused_append_refused(lib):
+def test_kivi_dtype_is_accepted(lib):
     P = ctypes.c_void_p
     k = _shape(kv_dtype=2)
     assert lib.gqa_paged_decode_workspace_size(ctypes.byref(k), 1000) > 0
-    call = lambda shape: lib.gqa_paged_decode_append_attention(
-        ctypes.byref(shape), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16),
+    # validation only (no launch): the fused step needs its new rows and the scales
+    call = lambda shape, kn, sc: lib.gqa_paged_decode_append_attention(
+        ctypes.byref(shape), P(16), P(kn), P(16), P(16), P(16), P(16), P(sc), P(sc), P(16),
         P(16), 100, 0.1, P(16), None, P(16), 1 << 30, None)
-    assert call(k) == 2
+    assert call(k, None, 16) == 1
+    assert call(k, 16, None) == 1
     assert lib.gqa_paged_decode_workspace_size(ctypes.byref(_shape(kv_dtype=3)), 1000) == 0

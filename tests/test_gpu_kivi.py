@@ -1,7 +1,7 @@
 """GPU checks of the KIVI fp8 layout (keys scaled per channel of each (block, KV
 head), values per token): attention parity against the float64 oracle over the
 same stored codes and scales, the quantising append bit for bit, append-then-
-attend steps, the block copy, and the fused append's refusal."""
+attend steps (separate and fused), and the block copy."""
 import numpy as np
 import pytest
 import torch
@@ -153,7 +153,7 @@ def test_kivi_decode_steps_append_then_attend(gpu):
                       ref, ref_lse, f"kivi step {step}")
 
 
-def test_kivi_block_copy_and_fused_refusal(gpu):
+def test_kivi_block_copy(gpu):
     rng = np.random.default_rng(11)
     nb, hkv, bs, d = 40, 4, 16, 64
     kp = rng.integers(0, 256, (nb, hkv, bs, d), dtype=np.uint8)
@@ -167,11 +167,62 @@ def test_kivi_block_copy_and_fused_refusal(gpu):
     gpu.kv_copy_blocks(dev[0], dev[1], _t(src), _t(dst), dev[2], dev[3])
     torch.cuda.synchronize()
     _same(tuple(x.cpu().numpy() for x in dev), ref, "kivi copy")
-    q = _t(_rows(rng, (1, 8, d), 1.0))
-    new = _t(_rows(rng, (1, hkv, d), 1.0))
-    with pytest.raises(gpu.GqaError) as e:
-        gpu.paged_decode_append_attention(q, new, new, _t(np.array([5], np.int32)), dev[0], dev[1],
-                                          _t(np.array([[0, 1]], np.int32)),
-                                          _t(np.array([6], np.int32)), 6, k_scale=dev[2],
-                                          v_scale=dev[3])
-    assert e.value.status == 2
+
+
+def _kivi_room(hq, hkv, d, bs, lens, extra, case_id):
+    spec = small_spec(num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      block_size=bs, kv_dtype="fp8_kivi", context=max(lens),
+                      pool="oversized2x", case_id=case_id)
+    case = make_case(spec, seed=4, context_lens=lens)
+    nb = case["k_pool_full"].shape[0]
+    tables = case["block_tables"]
+    used = set(tables[tables >= 0].tolist())
+    free = [i for i in range(nb) if i not in used]
+    grown = np.full((len(lens), -(-(max(lens) + extra) // bs)), -1, dtype=np.int32)
+    grown[:, :tables.shape[1]] = tables
+    for b, n in enumerate(lens):
+        for i in range(-(-n // bs), -(-(n + extra) // bs)):
+            grown[b, i] = free.pop()
+    return (case["k_pool_full"], case["v_pool_full"], case["k_scale"], case["v_scale"]), grown
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,nq", [(16, 4, 128, 16, 1), (64, 8, 128, 32, 1),
+                                            (8, 8, 64, 16, 1), (16, 8, 128, 32, 4),
+                                            (8, 8, 128, 16, 8)])
+def test_kivi_fused_append_and_attend(gpu, hq, hkv, d, bs, nq):
+    """Fused steps on a KIVI pool: the new tokens quantised with per-channel key and
+    per-token value scales inside the attention kernel (blocks spanning two wave
+    chunks included), codes and scales bit-exact after every step, parity on every
+    query position."""
+    lens = [700, 17, 2100]
+    steps = 6
+    state, grown = _kivi_room(hq, hkv, d, bs, lens, steps * nq, 9980 + hq + bs + nq)
+    dev = [_t(x) for x in state]
+    td = _t(grown)
+    rng = np.random.default_rng(hq + nq)
+    ctx = np.array(lens, dtype=np.int32)
+    for step in range(steps):
+        mags = 2.0 ** rng.uniform(-2, 3, (3, nq, hkv, d))
+        k_new, v_new = _rows(rng, (3, nq, hkv, d), mags), _rows(rng, (3, nq, hkv, d), mags)
+        state = oracle.kv_append_fp8(*state, k_new, v_new, grown, ctx, bs, layout="kivi")
+        start = ctx.copy()
+        ctx = ctx + nq
+        if nq == 1:
+            q = _rows(rng, (3, hq, d), 1.0)
+            out, lse = gpu.paged_decode_append_attention(
+                _t(q), _t(k_new[:, 0]), _t(v_new[:, 0]), _t(start), dev[0], dev[1], td, _t(ctx),
+                int(ctx.max()), d ** -0.5, k_scale=dev[2], v_scale=dev[3])
+            ref, ref_lse = oracle.paged_decode_attention(q, state[0], state[1], grown, ctx, bs,
+                                                         d ** -0.5, "fp8_kivi", state[2], state[3])
+        else:
+            q = _rows(rng, (3, nq, hq, d), 1.0)
+            out, lse = gpu.paged_decode_multi_query_append(
+                _t(q), _t(k_new), _t(v_new), dev[0], dev[1], td, _t(ctx), int(ctx.max()),
+                d ** -0.5, k_scale=dev[2], v_scale=dev[3])
+            ref, ref_lse = oracle.paged_multi_query_attention(q, state[0], state[1], grown, ctx, bs,
+                                                              d ** -0.5, "fp8_kivi", state[2],
+                                                              state[3])
+        torch.cuda.synchronize()
+        _same(tuple(x.cpu().numpy() for x in dev), state, f"kivi fused step {step}")
+        assert_parity(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                      ref, ref_lse, f"kivi fused step {step}")
