@@ -95,6 +95,24 @@ def fork_pairs(np, seed, first_block):
     return src, dst
 
 
+def identity_layout(case):
+    """Control-run layout, in place: the same contents with every sequence's blocks
+    stored one after another in logical order (then the unused blocks), so the
+    block table is the identity over the used blocks."""
+    import numpy as np
+    tab = case["block_tables"]
+    used = [int(x) for x in tab.reshape(-1) if x >= 0]
+    used_set = set(used)
+    rest = [i for i in range(case["k_pool"].shape[0]) if i not in used_set]
+    order = np.array(used + rest, dtype=np.int64)
+    for key in ("k_pool", "v_pool", "k_pool_full", "v_pool_full", "k_scale", "v_scale"):
+        if case.get(key) is not None:
+            case[key] = np.ascontiguousarray(case[key][order])
+    ident = np.full_like(tab, -1)
+    ident[tab >= 0] = np.arange(len(used), dtype=tab.dtype)
+    case["block_tables"] = ident
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gqa_decode_attention_paged_amd", "csrc")
@@ -169,15 +187,16 @@ def write_traffic(workload, pmc_dir, kv_bytes):
     print(json.dumps(out))
 
 
-def cpu_baseline(case, kv_bytes, min_seconds):
-    """Time the float64 oracle (as it stands) on whole steps of the workload, 1 BLAS thread."""
+def cpu_baseline(case, kv_bytes, min_seconds, threads=1):
+    """Time the float64 oracle (as it stands) on whole steps of the workload with
+    `threads` BLAS threads."""
     from threadpoolctl import threadpool_limits
     import oracle
     spec = case["spec"]
     fn = (oracle.paged_multi_query_attention if case.get("num_queries")
           else oracle.paged_decode_attention)
     n, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while True:
             kp, vp, ks, vs = (case["k_pool_full"], case["v_pool_full"], case["k_scale"],
                               case["v_scale"])
@@ -193,13 +212,13 @@ def cpu_baseline(case, kv_bytes, min_seconds):
             if el >= min_seconds:
                 break
     per_step = el / n
-    return {"value": round(kv_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
+    return {"value": round(kv_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} whole step(s) of the {spec.name} workload"
                       f"{' with the fp8 append' if 'fp8_k_new' in case else ''}"
                       f"{' with %d query positions' % case['num_queries'] if case.get('num_queries') else ''}"
                       ", float64 numpy oracle, "
-                      f"1 BLAS thread, {el:.1f} s total ({per_step * 1e3:.1f} ms/step)"}
+                      f"{threads} BLAS thread(s), {el:.1f} s total ({per_step * 1e3:.1f} ms/step)"}
 
 
 def main():
@@ -213,6 +232,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--identity-table", action="store_true",
+                    help="control run: the same data with each sequence's blocks stored "
+                         "contiguously and an identity block table (prices the gather)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -273,6 +295,8 @@ def main():
         case["fp8_start"] = (case["context_lens"] - 1).astype(np.int32)
     nq = case.get("num_queries", 1)
     kv_bytes = kv_bytes_per_step(spec, case["context_lens"])
+    if args.identity_table:
+        identity_layout(case)
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -358,6 +382,7 @@ def main():
             "block_size": spec.block_size, "kv_dtype": spec.kv_dtype,
             "context_lens_total": int(case["context_lens"].sum()), "append": spec.append,
             "query_positions": nq, "fp8_append": fp8_append,
+            "block_table": "identity (control run)" if args.identity_table else "random permutation",
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
         },
         "roofline": {
@@ -376,6 +401,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, kv_bytes, args.cpu_seconds)
+        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        result["cpu_baseline"]["all_cores"] = {
+            k: v for k, v in cpu_baseline(case, kv_bytes, args.cpu_seconds, cores).items()
+            if k in ("value", "cores", "sample")}
     print(json.dumps(result), flush=True)
 
 
