@@ -173,9 +173,10 @@ size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max
  * gqa_paged_decode_attention — one decode step of attention for B sequences.
  *   q             [B][H_q][d_h] bf16
  *   k_cache, v_cache  pools (layout above); bf16 or fp8 codes
- *   k_scale, v_scale  [num_blocks][H_kv] fp32 dequantisation scales for fp8
- *                 pools (value = decode(code) * scale[block][kv_head]); must
- *                 be NULL for bf16
+ *   k_scale, v_scale  fp32 dequantisation scales for fp8 pools (value =
+ *                 decode(code) * scale): [num_blocks][H_kv], or for
+ *                 GQA_KV_FP8_E4M3_KIVI k_scale [num_blocks][H_kv][d_h] and
+ *                 v_scale [num_blocks][H_kv][block_size]; must be NULL for bf16
  *   block_tables  [B][max_blocks_per_seq] int32
  *   context_lens  [B] int32: tokens each sequence attends, including a token
  *                 just appended; 0 gives out = 0, lse = -inf
@@ -319,12 +320,14 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t
 
 /*
  * gqa_kv_append_fp8 — append num_tokens (T) new tokens per sequence to an fp8
- * (E4M3) pool, quantising them with one fp32 scale per (block, KV head).
+ * (E4M3) pool, quantising them with one fp32 scale per (block, KV head), or
+ * with the KIVI layout (per-channel key scales, per-token value scales).
  *   k_new, v_new  [num_seqs][T][H_kv][head_dim] bf16 rows, finite (as are the
  *                 codes already in a block the call appends to)
  *   k_cache, v_cache  [num_blocks][H_kv][block_size][head_dim] E4M3 codes, and
- *   k_scale, v_scale  [num_blocks][H_kv] fp32 (value = decode(code) * scale):
- *                 modified in place at the blocks written
+ *   k_scale, v_scale  fp32 scales in the pool's layout (see gqa_kv_dtype;
+ *                 value = decode(code) * scale), modified in place at the
+ *                 blocks written
  *   block_tables  [num_seqs][max_blocks_per_seq] int32
  *   start_positions [num_seqs] int32: sequence b writes positions start[b] ..
  *                 start[b] + T - 1 (its current length upward); start < 0: none.
@@ -336,10 +339,14 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t
  * scale when that is >= t, and otherwise takes the smallest power of two >= t
  * and has its older codes re-encoded (exact while they stay normal E4M3).  New
  * values are encoded as round-to-nearest-even of clamp(x / scale, -448, 448).
+ * KIVI layout: keys follow this rule channel by channel (t, the scale and the
+ * re-encoding per channel of the tile); each value row gets the smallest power
+ * of two >= max|row| / 448 when it is written.
  * Precondition: no two sequences write the same block in one call.
  * Cites: *The Mathematics of Transformer Inference* §11 (x ~ s * round(x / s);
- * KV scales per head, per token); *Module 10*, "Quantise the cache, evaluate
- * the artifact" and the E4M3 row of its number-format table (largest value 448).
+ * KV scales per head, per token); *Module 10*, "Quantize the cache" (KIVI:
+ * per-channel keys, per-token values) and the E4M3 row of its number-format
+ * table (largest value 448).
  */
 gqa_status gqa_kv_append_fp8(const gqa_paged_shape* shape, int32_t num_tokens,
                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -353,8 +360,8 @@ gqa_status gqa_kv_append_fp8(const gqa_paged_shape* shape, int32_t num_tokens,
  * scales).  Used before a sequence writes into a block it shares with others
  * (reference counting and table updates are the caller's).
  *   k_cache, v_cache  pools, modified in place at the destination blocks
- *   k_scale, v_scale  [num_blocks][H_kv] fp32 for fp8 pools (copied along);
- *                 must be NULL for bf16
+ *   k_scale, v_scale  the fp8 pools' scales in their layout (see gqa_kv_dtype),
+ *                 copied along; must be NULL for bf16
  *   src_blocks, dst_blocks  [num_pairs] int32 device arrays; a pair with an id
  *                 outside [0, num_blocks), or with src == dst, copies nothing
  * A source may appear in several pairs (a fork copies one block several times).
