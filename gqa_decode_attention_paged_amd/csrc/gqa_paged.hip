@@ -255,7 +255,8 @@ static gqa_status append_impl(const gqa_paged_shape* s, int32_t num_tokens, cons
   if (num_tokens < 0 || num_tokens > 65535)
     return fail(GQA_ERR_INVALID_ARG, "num_tokens %d outside [0, 65535]", num_tokens);
   if (s->kv_dtype != GQA_KV_BF16)
-    return fail(GQA_ERR_UNSUPPORTED, "kv_append supports bf16 pools only");
+    return fail(GQA_ERR_UNSUPPORTED,
+                "kv_append copies bf16 rows; append to fp8 pools with gqa_kv_append_fp8");
   if (s->num_seqs == 0 || num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !positions)
     return fail(GQA_ERR_INVALID_ARG, "kv_append: NULL device pointer");

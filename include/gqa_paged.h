@@ -129,7 +129,8 @@ typedef struct gqa_paged_shape {
  * Writes k_cache[blk][h][pos % BS][:] = k_new[b][h][:] (same for V) with
  * blk = block_tables[b][pos / BS]; a bit-exact copy.  context_lens is not
  * touched: the caller passes the grown length to the attention call.
- * bf16 pools only (FP8 append returns GQA_ERR_UNSUPPORTED).
+ * bf16 pools only (GQA_ERR_UNSUPPORTED for fp8): fp8 pools are appended to,
+ * quantising, with gqa_kv_append_fp8.
  */
 gqa_status gqa_kv_append(const gqa_paged_shape* shape,
                          const void* k_new, const void* v_new,
@@ -146,7 +147,7 @@ gqa_status gqa_kv_append(const gqa_paged_shape* shape,
  *                 [0, max_blocks_per_seq * block_size) skips that token
  *   other arguments as gqa_kv_append, which is the T = 1 case.  Tokens are
  *   copied independently (bit-exact); two tokens given the same slot leave
- *   either one there.  bf16 pools only.
+ *   either one there.  bf16 pools only (fp8: gqa_kv_append_fp8).
  */
 gqa_status gqa_kv_append_tokens(const gqa_paged_shape* shape, int32_t num_tokens,
                                 const void* k_new, const void* v_new,
