@@ -251,6 +251,8 @@ struct CopyBlocksParams {
 // several copies; each copy reads it again, which the caches serve: the step is
 // bound by its writes, and small workgroups keep the most stores in flight
 // (reading a shared source once for a run of copies measured slower).
+typedef unsigned CopyUnit __attribute__((ext_vector_type(4)));   // 16 B
+
 __global__ __launch_bounds__(kCopyThreads) void kv_copy_blocks_kernel(CopyBlocksParams p) {
   const int src = p.src[blockIdx.x];
   const int dst = p.dst[blockIdx.x];
@@ -261,8 +263,13 @@ __global__ __launch_bounds__(kCopyThreads) void kv_copy_blocks_kernel(CopyBlocks
   if (off < p.block_bytes) {
     const uint4 kv = *reinterpret_cast<const uint4*>(p.k_cache + (size_t)src * p.block_bytes + off);
     const uint4 vv = *reinterpret_cast<const uint4*>(p.v_cache + (size_t)src * p.block_bytes + off);
-    *reinterpret_cast<uint4*>(p.k_cache + (size_t)dst * p.block_bytes + off) = kv;
-    *reinterpret_cast<uint4*>(p.v_cache + (size_t)dst * p.block_bytes + off) = vv;
+    // Non-temporal stores: the copy is bound by its writes, and the streaming hint
+    // takes a fork of 1,792 block pairs (32 KiB per pool) from 39 to 36 us.
+    // Non-temporal loads slow it down.
+    __builtin_nontemporal_store(__builtin_bit_cast(CopyUnit, kv),
+                                reinterpret_cast<CopyUnit*>(p.k_cache + (size_t)dst * p.block_bytes + off));
+    __builtin_nontemporal_store(__builtin_bit_cast(CopyUnit, vv),
+                                reinterpret_cast<CopyUnit*>(p.v_cache + (size_t)dst * p.block_bytes + off));
   }
   if (p.k_scale && blockIdx.y == 0) {
     for (int h = threadIdx.x; h < p.k_scales; h += kCopyThreads)
