@@ -56,6 +56,7 @@ def _pairs(rng, nb, n, invalid=True):
     ("fp8", 8, 16, 128, 300, 100),
     ("fp8", 40, 32, 64, 50, 20),
     ("bf16", 8, 16, 128, 9000, 4096),
+    ("bf16", 5, 16, 64, 60, 13),          # 10 KiB blocks: a partial last slice, 39 work items
 ])
 def test_copy_blocks_is_bit_exact(gpu, dt, hkv, bs, d, nb, n):
     rng = np.random.default_rng(nb + n + hkv)
