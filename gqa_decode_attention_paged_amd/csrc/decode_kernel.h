@@ -828,11 +828,16 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     const float l_wave = sum_swap32(sum_swap16(l_part));
     wave_bad = __any(bad);
     __syncthreads();                                 // staging area becomes sm_acc
+    // Every row below the capacity M is stored, under one branch instead of one
+    // per element: rows R..M-1 hold zeros (their weights are all zero) and are
+    // never read.  Lane group qd holds rows 4 qd .. 4 qd + 3.
+    if (4 * qd < M) {
 #pragma unroll
-    for (int n = 0; n < NN; ++n)
+      for (int n = 0; n < NN; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * qd + r < R) sm_acc(wave, 4 * qd + r, 16 * n + hd) = acc[n][r];
+        for (int r = 0; r < 4; ++r)
+          if (M >= 4 || r < M) sm_acc(wave, 4 * qd + r, 16 * n + hd) = acc[n][r];
+    }
     if (lane < R) {
       sm_m[wave][lane] = m_ref;
       sm_l[wave][lane] = l_wave;
