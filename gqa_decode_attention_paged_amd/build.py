@@ -17,6 +17,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from forming packed-FP32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # gfx950 preloads this many leading kernel-argument dwords into SGPRs (the
+    # decode kernel's block-table pointer, lengths pointer and plan scalars)
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = [os.path.join(CSRC, "gqa_paged.hip")]

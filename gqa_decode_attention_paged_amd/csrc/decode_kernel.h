@@ -59,14 +59,18 @@
 
 namespace gqa {
 
+// Kernel arguments other than the ones a workgroup's first loads depend on.
+// Those (the block tables, context lengths, the launch's length bound, the
+// table row length, the window and the split plan) come first as scalar
+// arguments: built with kernel-argument preloading, gfx950 places them in SGPRs
+// when a wave launches, so the block-id prefetch does not wait for the
+// argument segment to load.
 struct DecodeParams {
   const uint16_t* q;            // [B][Q][Hq][D] bf16
   void* k_cache;                // [NB][Hkv][BS][D]; written only by the fused append
   void* v_cache;
   float* k_scale;               // [NB][Hkv] (fp8 only); written only by the fused append
   float* v_scale;
-  const int32_t* block_tables;  // [B][max_blocks]
-  const int32_t* context_lens;  // [B]
   const uint16_t* k_new;        // fused append rows: [B][Hkv][D], or [B][Q][Hkv][D] with
   const uint16_t* v_new;        //   append_tail; else null
   const int32_t* positions;     // [B] slot of the appended token, or null
@@ -80,15 +84,9 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t group;                // G = num_q_heads / num_kv_heads (a power of two)
   int32_t group_shift;          // log2(G)
-  int32_t num_queries;          // Q query positions per sequence (the last Q tokens)
   int32_t rows;                 // R = G * Q rows per (sequence, KV head)
-  int32_t window;               // sliding window w (0: attend to the whole context)
   int32_t num_blocks;
-  int32_t max_blocks;
   int32_t max_splits;           // row stride of the split partials
-  int32_t hint_ctx;             // host bound on context lengths (sizes the grid)
-  int32_t target_splits;        // split-count target of the split plan
-  int32_t proportional;         // slots shared out by sequence length (2 <= B <= 64)
   float scale_log2;             // softmax_scale * log2(e)
 };
 
@@ -185,11 +183,12 @@ __device__ __forceinline__ void widen8(const typename KVTraits<FP8>::Vec& v, flo
 }
 
 // Copy the appended token's K and V rows of (b, kvh) into the cache (bf16 pools).
-__device__ __forceinline__ void append_rows(const DecodeParams& p, int b, int kvh, int pos, int D,
+__device__ __forceinline__ void append_rows(const DecodeParams& p, const int32_t* block_tables,
+                                            int max_blocks, int b, int kvh, int pos, int D,
                                             int BS) {
   const int units = D / 8;
-  if ((int)threadIdx.x >= units || pos < 0 || pos >= p.max_blocks * BS) return;
-  const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / BS];
+  if ((int)threadIdx.x >= units || pos < 0 || pos >= max_blocks * BS) return;
+  const int blk = block_tables[(size_t)b * max_blocks + pos / BS];
   if (blk < 0 || blk >= p.num_blocks) return;
   const size_t src = ((size_t)b * p.num_kv_heads + kvh) * D + threadIdx.x * 8;
   const size_t dst = (((size_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * D + threadIdx.x * 8;
@@ -261,8 +260,19 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
 template <int D, int BS, int M, int KV, int WAVES>
 // Launch bounds ask for two resident waves per SIMD (one 8-wave or two 4-wave
 // workgroups per CU), which caps registers at 256 per lane.
-__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(DecodeParams p) {
+//
+// block_tables [B][max_blocks]; context_lens [B]; hint_ctx: the host's bound on
+// the context lengths (it sizes the grid); window: sliding window w (0: the
+// whole context); plan_flags: the split-count target in bits 0-7, bit 8 set
+// when slots are shared out by sequence length (2 <= B <= 64), and in bits
+// 16-23 the number Q of query positions per sequence (its last Q tokens).
+__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int32_t hint_ctx, int32_t max_blocks, int32_t window, int32_t plan_flags, DecodeParams p) {
   constexpr bool FP8 = KV != 0;
+  const int target_splits = plan_flags & 0xff;
+  const bool proportional = (plan_flags & 0x100) != 0;
+  const int Q = (plan_flags >> 16) & 0xff;   // query positions per sequence
   constexpr bool KIVI = KV == 2;
   // M is the row capacity: the rows of one (sequence, KV head) are its query
   // positions times its G query heads, row m = i*G + g (R = G*Q <= M of them).
@@ -307,7 +317,6 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   const int S = gridDim.x;
   const int kvh = blockIdx.y;
   const int G = p.group;                     // query heads per KV head
-  const int Q = p.num_queries;               // query positions per sequence
   const int R = p.rows;                      // rows in use, G*Q
   const int h0 = kvh * G;
 
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // launch hint's length, where slot (x, z) is split x of sequence z under the
   // hint's split plan; the ids of this wave's chunks there are loaded together
   // with the context lengths.
-  const int32_t* bt = p.block_tables + (size_t)blockIdx.z * p.max_blocks;
+  const int32_t* bt = block_tables + (size_t)blockIdx.z * max_blocks;
   auto load_ids = [&](int s0_, int s1_, int my_n_, int jbase) {
     const int jj = jbase + lane / EPC;
     const int tok = s0_ + (wave + jj * WAVES) * CT + (lane % EPC) * BS;
@@ -352,14 +361,14 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // from the start of the block holding the first token any of its queries
   // sees: blocks wholly before the window are never read.
   auto span_base = [&](int c) {
-    if (p.window <= 0) return 0;
-    const int first = c - p.num_queries + 1 - p.window;      // query 0's first token
+    if (window <= 0) return 0;
+    const int first = c - Q + 1 - window;                  // query 0's first token
     return first > 0 ? first / BS * BS : 0;
   };
-  const int hbase = span_base(p.hint_ctx);
-  const SplitPlan hplan = split_plan(p.hint_ctx - hbase, p.target_splits);
+  const int hbase = span_base(hint_ctx);
+  const SplitPlan hplan = split_plan(hint_ctx - hbase, target_splits);
   const int hs0 = hbase + (int)blockIdx.x * hplan.split_tokens;
-  const int hs1 = min(p.hint_ctx, hs0 + hplan.split_tokens);
+  const int hs1 = min(hint_ctx, hs0 + hplan.split_tokens);
   const int hmy_n = (int)blockIdx.x < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
   int ids = load_ids(hs0, hs1, hmy_n, 0);
 
@@ -373,7 +382,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // 512-8192 tokens the step drops from 55.3 to 52.0 us (a paged gather by a
   // lone workgroup measured 55 GB/s with the hint against 88 without).
   int stream_tokens = INT_MAX;
-  if (p.proportional) {
+  if (proportional) {
     // Lane i holds sequence i.  When the lengths differ, sequence i gets
     // n_i = 1 + floor(R c_i / sum c) slots (invalid lengths weigh 0), R the
     // largest value in [S*B - B, S*B] for which the n_i fit the S*B slots.
@@ -381,11 +390,11 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     // depend on the batch order.  Equal lengths keep the uniform plan (which
     // the sharing would also give: n_i = S).
     const int nseq = gridDim.z;
-    const int ci = lane < nseq ? p.context_lens[lane] : 0;
+    const int ci = lane < nseq ? context_lens[lane] : 0;
     const int pi = (p.positions && lane < nseq) ? p.positions[lane] : -1;
     const int c0 = __builtin_amdgcn_readfirstlane(ci);
     if (__ballot(lane < nseq && ci != c0) != 0) {    // lengths differ: share out
-      const int cw = (ci > 0 && ci <= p.hint_ctx && ci <= p.max_blocks * BS) ? ci - span_base(ci) : 0;
+      const int cw = (ci > 0 && ci <= hint_ctx && ci <= max_blocks * BS) ? ci - span_base(ci) : 0;
       const double tot = wave_sum_f64((double)cw);
       const double f = tot > 0.0 ? (double)cw / tot : 0.0;
       const int slots = S * nseq;
@@ -409,20 +418,20 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       if (b >= nseq) return;                         // a slot the rounding left over
       split = slot - (b > 0 ? __builtin_amdgcn_readlane(incl, b - 1) : 0);
       slots_b = __builtin_amdgcn_readlane(ni, b);
-      bt = p.block_tables + (size_t)b * p.max_blocks;
+      bt = block_tables + (size_t)b * max_blocks;
     }
     ctx = __builtin_amdgcn_readlane(ci, b);
     pos = __builtin_amdgcn_readlane(pi, b);
   } else {
-    ctx = p.context_lens[b];
+    ctx = context_lens[b];
     pos = p.positions ? p.positions[b] : -1;
   }
   // A sequence holds its Q query positions as its last Q tokens, so 0 < ctx < Q
   // is invalid (ctx = 0 stays the empty sequence).
-  const bool ctx_bad = ctx < 0 || ctx > p.max_blocks * BS || (ctx > 0 && ctx < Q);
+  const bool ctx_bad = ctx < 0 || ctx > max_blocks * BS || (ctx > 0 && ctx < Q);
   const int base = ctx_bad ? 0 : span_base(ctx);    // first token of the attended span
   const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx - base,
-                                    p.proportional ? slots_b : p.target_splits);
+                                    proportional ? slots_b : target_splits);
   // Row m of this (sequence, KV head) is query i = m / G of head h0 + m % G; its
   // flat index into q [B][Q][H_q][D], out and out_lse.  Query i sits at position
   // ctx - Q + i and attends to the tokens before it and itself.
@@ -431,9 +440,9 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   };
   auto row_limit = [&](int m) { return ctx - Q + 1 + (m >> p.group_shift); };   // tokens < this
   auto row_low = [&](int m) {                      // and tokens >= this (sliding window)
-    return p.window > 0 ? max(0, row_limit(m) - p.window) : 0;
+    return window > 0 ? max(0, row_limit(m) - window) : 0;
   };
-  const bool too_long = ctx > p.hint_ctx || plan.num_splits > slots_b ||
+  const bool too_long = ctx > hint_ctx || plan.num_splits > slots_b ||
                         plan.num_splits > p.max_splits;
   const bool degenerate = ctx_bad || too_long || plan.num_splits == 0;
   const bool pos_in_split = !degenerate && pos >= base && pos < ctx;
@@ -454,13 +463,13 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   };
   if (p.positions && split == owner && !pos_in_split) {
     if constexpr (FP8) {
-      if (wave == 0 && pos >= 0 && pos < p.max_blocks * BS) {
-        const int blk = p.block_tables[(size_t)b * p.max_blocks + pos / BS];
+      if (wave == 0 && pos >= 0 && pos < max_blocks * BS) {
+        const int blk = block_tables[(size_t)b * max_blocks + pos / BS];
         if ((unsigned)blk < (unsigned)p.num_blocks)
           append_fp8_tile(blk, pos % BS, 1, ((size_t)b * p.num_kv_heads + kvh) * D, 0);
       }
     } else {
-      append_rows(p, b, kvh, pos, D, BS);
+      append_rows(p, block_tables, max_blocks, b, kvh, pos, D, BS);
     }
   }
 

@@ -407,8 +407,6 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   // Written only by a fused fp8 append, whose entry points take them non-const.
   p.k_scale = const_cast<float*>(k_scale);
   p.v_scale = const_cast<float*>(v_scale);
-  p.block_tables = block_tables;
-  p.context_lens = context_lens;
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
   p.positions = positions;
@@ -422,19 +420,23 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.num_kv_heads = s->num_kv_heads;
   p.group = G;
   p.group_shift = __builtin_ctz((unsigned)G);
-  p.num_queries = num_queries;
   p.rows = rows;
   p.num_blocks = s->num_blocks;
-  p.max_blocks = s->max_blocks_per_seq;
   p.max_splits = ws_splits;
-  p.window = s->sliding_window;
-  p.hint_ctx = max_context_len;
-  p.target_splits = target;
-  p.proportional = proportional ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  st = launch(fn, dim3(launch_splits, s->num_kv_heads, s->num_seqs), dim3(waves * 64), &p,
-              "paged_decode", stream);
-  return st == GQA_OK ? ok() : st;
+  // The leading scalar arguments of paged_decode_kernel (preloaded into SGPRs).
+  const int32_t* bt_arg = block_tables;
+  const int32_t* lens_arg = context_lens;
+  int32_t hint_arg = max_context_len;
+  int32_t max_blocks_arg = s->max_blocks_per_seq;
+  int32_t window_arg = s->sliding_window;
+  int32_t plan_arg = target | (proportional ? 1 << 8 : 0) | num_queries << 16;
+  void* args[] = {&bt_arg, &lens_arg, &hint_arg, &max_blocks_arg, &window_arg, &plan_arg, &p};
+  const hipError_t e = hipLaunchKernel(fn, dim3(launch_splits, s->num_kv_heads, s->num_seqs),
+                                       dim3(waves * 64), args, 0, stream);
+  if (e != hipSuccess)
+    return fail(GQA_ERR_HIP, "paged_decode launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 gqa_status gqa_paged_decode_attention(const gqa_paged_shape* s, const void* q,
