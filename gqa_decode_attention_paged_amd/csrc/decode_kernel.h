@@ -61,10 +61,10 @@ namespace gqa {
 
 // Kernel arguments other than the ones a workgroup's first loads depend on.
 // Those (the block tables, context lengths, the launch's length bound, the
-// table row length, the window and the split plan) come first as scalar
+// table row length, the window, the split target and Q) come first as scalar
 // arguments: built with kernel-argument preloading, gfx950 places them in SGPRs
-// when a wave launches, so the block-id prefetch does not wait for the
-// argument segment to load.
+// when a wave launches, so the block-id prefetch and the length load do not
+// wait for the argument segment to load.
 struct DecodeParams {
   const uint16_t* q;            // [B][Q][Hq][D] bf16
   void* k_cache;                // [NB][Hkv][BS][D]; written only by the fused append
@@ -87,6 +87,7 @@ struct DecodeParams {
   int32_t rows;                 // R = G * Q rows per (sequence, KV head)
   int32_t num_blocks;
   int32_t max_splits;           // row stride of the split partials
+  int32_t proportional;         // slots shared out by sequence length (2 <= B <= 64)
   float scale_log2;             // softmax_scale * log2(e)
 };
 
@@ -271,7 +272,6 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     int32_t hint_ctx, int32_t max_blocks, int32_t window, int32_t plan_flags, DecodeParams p) {
   constexpr bool FP8 = KV != 0;
   const int target_splits = plan_flags & 0xff;
-  const bool proportional = (plan_flags & 0x100) != 0;
   const int Q = (plan_flags >> 16) & 0xff;   // query positions per sequence
   constexpr bool KIVI = KV == 2;
   // M is the row capacity: the rows of one (sequence, KV head) are its query
@@ -279,6 +279,11 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // bf16 pools with two or more rows use the matrix path; fp8 pools and single
   // rows the vector path.
   constexpr bool MFMA = !FP8 && M >= 2;
+  // Slots shared out by sequence length.  The matrix path branches on the
+  // preloaded copy of the flag (bit 8 of plan_flags), so the uniform path does
+  // not wait for the argument segment; on the vector path that copy costs 16-34
+  // VGPRs, enough to halve its occupancy, so it reads the one in p.
+  const bool proportional = MFMA ? (plan_flags & 0x100) != 0 : p.proportional != 0;
   constexpr int LPT = D / 8;                 // lanes per token row (8 elements each)
   constexpr int TPI = kWave / LPT;           // rows per row-layout load instruction
   constexpr int CT = (MFMA || M < 8) ? 32 : 16;   // tokens per wave chunk

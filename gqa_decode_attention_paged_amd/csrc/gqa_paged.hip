@@ -423,6 +423,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.rows = rows;
   p.num_blocks = s->num_blocks;
   p.max_splits = ws_splits;
+  p.proportional = proportional ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   // The leading scalar arguments of paged_decode_kernel (preloaded into SGPRs).
   const int32_t* bt_arg = block_tables;
