@@ -63,8 +63,8 @@ namespace gqa {
 // Those (the block tables, context lengths, the launch's length bound, the
 // table row length, the window, the split target and Q) come first as scalar
 // arguments: built with kernel-argument preloading, gfx950 places them in SGPRs
-// when a wave launches, so the block-id prefetch and the length load do not
-// wait for the argument segment to load.
+// when a wave launches, so the block-id prefetch (and, on the matrix path, the
+// length load) does not wait for the argument segment to load.
 struct DecodeParams {
   const uint16_t* q;            // [B][Q][Hq][D] bf16
   void* k_cache;                // [NB][Hkv][BS][D]; written only by the fused append
