@@ -123,6 +123,83 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _dtypes(kind):
+    import torch
+    bf16 = (torch.bfloat16, torch.int16, torch.uint16)
+    return {"bf16": bf16, "pool": bf16 + (torch.uint8, torch.float8_e4m3fn),
+            "i32": (torch.int32,), "f32": (torch.float32,)}[kind]
+
+
+class _Checks:
+    """Checks of the tensor arguments of one call, before any pointer crosses the
+    boundary.  The kernels index raw device memory by the sizes they are given,
+    so a tensor of another dtype, size or layout, or one in host memory, would
+    be read out of bounds instead of rejected.  Each call checks dtype, shape
+    and layout per tensor, then (``on_gpu``) that all of them are in GPU memory."""
+
+    def __init__(self):
+        self.seen = []
+
+    def __call__(self, t, name, kind=None, shape=None, min_rows=None):
+        """``shape`` is the exact shape; ``min_rows`` a lower bound on the first
+        dimension (tables and lengths may cover more sequences than the call uses)."""
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if kind is not None and t.dtype not in _dtypes(kind):
+            names = " or ".join(str(d).replace("torch.", "") for d in _dtypes(kind))
+            raise TypeError(f"{name}: expected {names}, got {str(t.dtype).replace('torch.', '')}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+        if min_rows is not None and (t.dim() == 0 or t.shape[0] < min_rows):
+            raise ValueError(f"{name}: needs at least {min_rows} rows, got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.seen.append((name, t))
+        return t
+
+    def on_gpu(self):
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be in GPU memory, got {t.device}")
+
+
+def _pools(chk, k_cache, v_cache, k_scale=None, v_scale=None):
+    """The two pools: same dtype and [NB][H_kv][BS][d_h] shape; fp8 scales, when
+    given, float32 in the per-(block, head) or KIVI layout."""
+    chk(k_cache, "k_cache", "pool")
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache: expected [num_blocks][H_kv][block_size][d_h], got "
+                         f"shape {tuple(k_cache.shape)}")
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError(f"v_cache: expected {k_cache.dtype} like k_cache, got {v_cache.dtype}")
+    chk(v_cache, "v_cache", shape=k_cache.shape)
+    nb, hkv, bs, d = k_cache.shape
+    kivi = _kv_dtype(k_cache, k_scale) == GQA_KV_FP8_E4M3_KIVI
+    if k_scale is not None:
+        chk(k_scale, "k_scale", "f32", (nb, hkv, d) if kivi else (nb, hkv))
+    if v_scale is not None:
+        chk(v_scale, "v_scale", "f32", (nb, hkv, bs) if kivi else (nb, hkv))
+    return nb, hkv, bs, d
+
+
+def _attention_args(chk, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                    out, out_lse, workspace):
+    """Common checks of the attention entry points; q is [B](Q)[H_q][d_h]."""
+    chk(q, "q", "bf16")
+    _, _, _, d = _pools(chk, k_cache, v_cache, k_scale, v_scale)
+    if q.shape[-1] != d:
+        raise ValueError(f"q: head dim {q.shape[-1]} differs from the pools' {d}")
+    B = q.shape[0]
+    chk(block_tables, "block_tables", "i32", min_rows=B)
+    if block_tables.dim() != 2:
+        raise ValueError(f"block_tables: expected [B][max_blocks], got {tuple(block_tables.shape)}")
+    chk(context_lens, "context_lens", "i32", min_rows=B)
+    chk(out, "out", "f32", tuple(q.shape))
+    if out_lse is not None:
+        chk(out_lse, "out_lse", "f32", tuple(q.shape[:-1]))
+    chk(workspace, "workspace")
+
+
 def _stream(t):
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -160,8 +237,16 @@ def workspace_size(shape: PagedShape, max_context_len: int) -> int:
 
 def kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions):
     """Write one new token per sequence into the paged pools (in place)."""
+    chk = _Checks()
     lib = load()
-    shape = make_shape(k_new.shape[0], k_cache.shape[1], k_cache, block_tables)
+    _, hkv, _, d = _pools(chk, k_cache, v_cache)
+    B = k_new.shape[0]
+    chk(k_new, "k_new", "bf16", (B, hkv, d))
+    chk(v_new, "v_new", "bf16", (B, hkv, d))
+    chk(block_tables, "block_tables", "i32", min_rows=B)
+    chk(positions, "positions", "i32", min_rows=B)
+    shape = make_shape(B, hkv, k_cache, block_tables)
+    chk.on_gpu()
     _check(lib.gqa_kv_append(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                              _ptr(v_cache), _ptr(block_tables), _ptr(positions),
                              _stream(k_cache)))
@@ -169,9 +254,16 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions):
 
 def kv_append_tokens(k_new, v_new, k_cache, v_cache, block_tables, positions):
     """Write T new tokens per sequence ([B][T][H_kv][d_h] rows at positions [B][T])."""
+    chk = _Checks()
     lib = load()
+    _, hkv, _, d = _pools(chk, k_cache, v_cache)
     B, T = k_new.shape[0], k_new.shape[1]
-    shape = make_shape(B, k_cache.shape[1], k_cache, block_tables)
+    chk(k_new, "k_new", "bf16", (B, T, hkv, d))
+    chk(v_new, "v_new", "bf16", (B, T, hkv, d))
+    chk(block_tables, "block_tables", "i32", min_rows=B)
+    chk(positions, "positions", "i32", (B, T))
+    shape = make_shape(B, hkv, k_cache, block_tables)
+    chk.on_gpu()
     _check(lib.gqa_kv_append_tokens(ctypes.byref(shape), int(T), _ptr(k_new), _ptr(v_new),
                                     _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                     _ptr(positions), _stream(k_cache)))
@@ -189,6 +281,7 @@ def paged_decode_multi_query(q, k_cache, v_cache, block_tables, context_lens, ma
     """Attention for Q consecutive query positions per sequence, q [B][Q][H_q][d_h]: query i
     sits at position context_lens[b] - Q + i and attends causally.  Returns (out, lse)."""
     import torch
+    chk = _Checks()
     lib = load()
     B, Q, Hq, D = q.shape
     shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
@@ -201,6 +294,9 @@ def paged_decode_multi_query(q, k_cache, v_cache, block_tables, context_lens, ma
     if workspace is None:
         nbytes = multi_query_workspace_size(shape, Q, max_context_len)
         workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _attention_args(chk, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                    out_lse, workspace)
+    chk.on_gpu()
     _check(lib.gqa_paged_decode_multi_query(
         ctypes.byref(shape), int(Q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
@@ -214,6 +310,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
                            out_lse=None, workspace=None, return_lse=True, batch_invariant=False, sliding_window=0):
     """Decode attention for a batch; returns (out, lse) (lse None if not requested)."""
     import torch
+    chk = _Checks()
     lib = load()
     B, Hq, D = q.shape
     shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
@@ -225,6 +322,9 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
         out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = make_workspace(shape, max_context_len, q.device)
+    _attention_args(chk, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                    out_lse, workspace)
+    chk.on_gpu()
     _check(lib.gqa_paged_decode_attention(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
@@ -242,6 +342,7 @@ def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tab
     context_lens[b] - Q + i, then attend for the Q positions (one kernel).  fp8
     pools: the rows are quantised into them and k_scale/v_scale updated."""
     import torch
+    chk = _Checks()
     lib = load()
     B, Q, Hq, D = q.shape
     shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
@@ -254,6 +355,11 @@ def paged_decode_multi_query_append(q, k_new, v_new, k_cache, v_cache, block_tab
     if workspace is None:
         nbytes = multi_query_workspace_size(shape, Q, max_context_len)
         workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _attention_args(chk, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                    out_lse, workspace)
+    chk(k_new, "k_new", "bf16", (B, Q, k_cache.shape[1], D))
+    chk(v_new, "v_new", "bf16", (B, Q, k_cache.shape[1], D))
+    chk.on_gpu()
     _check(lib.gqa_paged_decode_multi_query_append(
         ctypes.byref(shape), int(Q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
         _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
@@ -278,6 +384,7 @@ def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, 
     """Fused decode step: commit the new token at positions[b], then attend (one kernel).
     fp8 pools: the row is quantised into them and k_scale/v_scale updated."""
     import torch
+    chk = _Checks()
     lib = load()
     B, Hq, D = q.shape
     shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
@@ -289,6 +396,12 @@ def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, 
         out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = make_workspace(shape, max_context_len, q.device)
+    _attention_args(chk, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                    out_lse, workspace)
+    chk(k_new, "k_new", "bf16", (B, k_cache.shape[1], D))
+    chk(v_new, "v_new", "bf16", (B, k_cache.shape[1], D))
+    chk(positions, "positions", "i32", min_rows=B)
+    chk.on_gpu()
     _check(lib.gqa_paged_decode_append_attention(
         ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(k_cache),
         _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
@@ -300,6 +413,9 @@ def paged_decode_append_attention(q, k_new, v_new, positions, k_cache, v_cache, 
 
 def workspace_init(shape: PagedShape, max_context_len: int, workspace):
     """Zero a workspace's arrival counters on the current stream."""
+    chk = _Checks()
+    chk(workspace, "workspace")
+    chk.on_gpu()
     _check(load().gqa_paged_decode_workspace_init(
         ctypes.byref(shape), int(max_context_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(workspace)))
@@ -311,11 +427,18 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables
     (one token) or [B][T][H_kv][d_h] at positions start_positions[b] + j (in place,
     scales included).  Scales [NB][H_kv] (per (block, head)) or the KIVI layout
     (k_scale [NB][H_kv][d_h], v_scale [NB][H_kv][BS])."""
+    chk = _Checks()
     lib = load()
     if k_new.dim() == 3:
         k_new, v_new = k_new.unsqueeze(1), v_new.unsqueeze(1)
     B, T = k_new.shape[0], k_new.shape[1]
-    shape = make_shape(B, k_cache.shape[1], k_cache, block_tables, k_scale=k_scale)
+    _, hkv, _, d = _pools(chk, k_cache, v_cache, k_scale, v_scale)
+    chk(k_new, "k_new", "bf16", (B, T, hkv, d))
+    chk(v_new, "v_new", "bf16", (B, T, hkv, d))
+    chk(block_tables, "block_tables", "i32", min_rows=B)
+    chk(start_positions, "start_positions", "i32", min_rows=B)
+    shape = make_shape(B, hkv, k_cache, block_tables, k_scale=k_scale)
+    chk.on_gpu()
     _check(lib.gqa_kv_append_fp8(ctypes.byref(shape), int(T), _ptr(k_new), _ptr(v_new),
                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(block_tables), _ptr(start_positions), _stream(k_cache)))
@@ -324,8 +447,12 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables
 def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_scale=None):
     """Copy-on-write block copy: block dst_blocks[j] of both pools (and the fp8 scales)
     becomes a copy of src_blocks[j], in place."""
-    nb, hkv, bs, d = k_cache.shape
+    chk = _Checks()
+    nb, hkv, bs, d = _pools(chk, k_cache, v_cache, k_scale, v_scale)
+    chk(src_blocks, "src_blocks", "i32")
+    chk(dst_blocks, "dst_blocks", "i32", shape=src_blocks.shape)
     shape = PagedShape(1, hkv, hkv, d, bs, nb, 1, _kv_dtype(k_cache, k_scale), 0, 0)
+    chk.on_gpu()
     _check(load().gqa_kv_copy_blocks(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(k_scale), _ptr(v_scale), _ptr(src_blocks),
                                      _ptr(dst_blocks), int(src_blocks.numel()),
@@ -334,12 +461,16 @@ def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_sca
 
 def kv_gather(cache, block_tables, seq, num_tokens):
     """Copy sequence ``seq``'s first ``num_tokens`` rows out of a pool: [H_kv][T][d_h]."""
+    chk = _Checks()
     import torch
     lib = load()
+    chk(cache, "cache", "pool")
+    chk(block_tables, "block_tables", "i32")
     nb, hkv, bs, d = cache.shape
     shape = PagedShape(block_tables.shape[0], hkv, hkv, d, bs, nb, block_tables.shape[1],
                        _kv_dtype(cache), 0, 0)
     out = torch.empty((hkv, num_tokens, d), dtype=cache.dtype, device=cache.device)
+    chk.on_gpu()
     _check(lib.gqa_kv_gather(ctypes.byref(shape), _ptr(cache), _ptr(block_tables), int(seq),
                              int(num_tokens), _ptr(out), _stream(cache)))
     return out
