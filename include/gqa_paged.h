@@ -366,6 +366,8 @@ gqa_status gqa_kv_append_fp8(const gqa_paged_shape* shape, int32_t num_tokens,
  *   src_blocks, dst_blocks  [num_pairs] int32 device arrays; a pair with an id
  *                 outside [0, num_blocks), or with src == dst, copies nothing
  * A source may appear in several pairs (a fork copies one block several times).
+ * Performance only: pairs sharing a source are best listed next to each other,
+ * as a fork produces them; the copies then read it through one XCD's L2.
  * Precondition: no block is the destination of two pairs or both a source and
  * a destination in one call (the copies run concurrently).
  * Cites: *Module 10*, "Share only state with the same identity"; *Stochastic
