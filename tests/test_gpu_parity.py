@@ -114,6 +114,20 @@ def test_ragged_batch_at_the_lane_limit(gpu, nseq):
     assert_parity(out, lse, ref, ref_lse, f"{nseq} sequences")
 
 
+@pytest.mark.parametrize("dt,hq", [("bf16", 32), ("bf16", 8), ("fp8", 8), ("fp8_kivi", 8)])
+def test_ragged_batch_on_four_wave_workgroups(gpu, dt, hq):
+    """Ragged batches whose 8-wave plan gives each sequence at most two splits run
+    on 4-wave workgroups (twice the slots to share out by length): the matrix path
+    (G = 4) and the vector path (G = 1) on bf16, fp8 and KIVI pools."""
+    lens = np.random.default_rng(24).integers(1, 1500, 24).tolist()
+    spec = small_spec(num_seqs=24, num_q_heads=hq, num_kv_heads=8, head_dim=128, block_size=16,
+                      kv_dtype=dt, context=1500, case_id=2950 + hq + len(dt))
+    case = make_case(spec, seed=12, context_lens=lens)
+    ref, ref_lse = run_oracle(case)
+    out, lse = run_step(gpu, to_device(case), case)
+    assert_parity(out, lse, ref, ref_lse, f"24 ragged sequences, {dt}, H_q {hq}")
+
+
 def test_ragged_batch_with_invalid_lengths(gpu):
     """Invalid lengths inside a ragged batch: those sequences get NaN (negative, or
     longer than the launch hint), an empty one gets zeros, the rest match the oracle."""
