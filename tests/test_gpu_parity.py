@@ -146,12 +146,15 @@ def test_ragged_batch_with_invalid_lengths(gpu):
     assert_parity(out[keep], lse[keep], ref[keep], ref_lse[keep], "valid sequences")
 
 
-def test_fused_append_ragged_batch(gpu):
+@pytest.mark.parametrize("lens", [
+    [3000, 17, 700, 1, 2048, 129],
+    [int(n) for n in np.random.default_rng(31).integers(1, 2000, 24)],   # 4-wave workgroups
+], ids=["6 sequences", "24 sequences"])
+def test_fused_append_ragged_batch(gpu, lens):
     """The fused append with a ragged batch: each sequence's new token is committed by
     the workgroup that owns its slot, and attention matches the oracle."""
-    lens = [3000, 17, 700, 1, 2048, 129]
     spec = small_spec(num_seqs=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
-                      block_size=16, context=max(lens), append=True, case_id=3100)
+                      block_size=16, context=max(lens), append=True, case_id=3100 + len(lens))
     case = make_case(spec, seed=13, context_lens=lens)
     ref, ref_lse = run_oracle(case)
     dev = to_device(case)
