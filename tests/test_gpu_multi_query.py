@@ -62,6 +62,19 @@ def test_multi_query_parity(gpu, hq, hkv, nq, d, bs, dt):
         assert np.array_equal(k, case["k_pool_full"])
 
 
+@pytest.mark.parametrize("hq,nq,dt", [(32, 4, "bf16"), (8, 2, "bf16"), (8, 4, "fp8")])
+def test_multi_query_ragged_on_four_wave_workgroups(gpu, hq, nq, dt):
+    """24 ragged sequences x 8 KV heads: the 8-wave plan gives each at most two
+    splits, so the call runs on 4-wave workgroups sharing slots out by length."""
+    lens = [int(n) for n in np.random.default_rng(nq).integers(nq, 1500, 24)]
+    spec = small_spec(num_seqs=24, num_q_heads=hq, num_kv_heads=8, head_dim=128,
+                      block_size=16, kv_dtype=dt, context=1500, case_id=6700 + hq + nq)
+    case = make_multi_query_case(spec, nq, seed=5, context_lens=lens, append=(dt == "bf16"))
+    ref, ref_lse = _reference(case)
+    out, lse = _verify_step(gpu, case, to_device(case))
+    assert_parity(out, lse, ref, ref_lse, f"24 ragged sequences, G={hq // 8} Q={nq} {dt}")
+
+
 def test_single_position_matches_the_decode_entry_point_bitwise(gpu):
     spec = small_spec(num_seqs=3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                       context=2000, case_id=6100)
