@@ -70,6 +70,18 @@ def test_window_parity(gpu, hq, hkv, d, bs, dt, nq, w):
     assert_parity(out, lse, ref, ref_lse, f"w={w} Q={nq} G={hq // hkv} {dt}")
 
 
+def test_window_on_four_wave_workgroups(gpu):
+    """A window over 24 ragged sequences x 8 KV heads (4-wave workgroups sharing
+    slots out by each sequence's attended span)."""
+    lens = [int(n) for n in np.random.default_rng(77).integers(1, 3000, 24)]
+    spec = small_spec(num_seqs=24, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context=3000, case_id=8077)
+    case = make_case(spec, seed=2, context_lens=lens)
+    ref, ref_lse = _ref(case, 300)
+    out, lse = _run(gpu, case, to_device(case), 300)
+    assert_parity(out, lse, ref, ref_lse, "w=300, 24 ragged sequences")
+
+
 @pytest.mark.parametrize("nq", [1, 3])
 def test_blocks_before_the_window_are_never_read(gpu, nq):
     """Table entries of blocks wholly before every query's window are set to -1 and
