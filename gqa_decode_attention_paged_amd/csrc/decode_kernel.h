@@ -380,12 +380,12 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // This workgroup's sequence b, its split, and the number of slots b owns.
   int b = blockIdx.z, split = blockIdx.x, slots_b = S, ctx, pos;
   // Tokens of the split read with the non-temporal hint (the rest with the
-  // default policy): all of them, except in a ragged batch, where only the
-  // average slot's share is.  The hint pays while every workgroup streams, but
-  // a split longer than the average reads its remainder after most workgroups
-  // have finished, and there the default policy is faster: on 16 sequences of
-  // 512-8192 tokens the step drops from 55.3 to 52.0 us (a paged gather by a
-  // lone workgroup measured 55 GB/s with the hint against 88 without).
+  // default policy): in a ragged batch at most the average slot's share.  The
+  // hint pays while every workgroup streams, but a split longer than the
+  // average reads its remainder after most workgroups have finished, and there
+  // the default policy is faster: on 16 sequences of 512-8192 tokens the step
+  // drops from 55.3 to 52.0 us (a paged gather by a lone workgroup measured
+  // 55 GB/s with the hint against 88 without).
   int stream_tokens = INT_MAX;
   if (proportional) {
     // Lane i holds sequence i.  When the lengths differ, sequence i gets
@@ -437,6 +437,10 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   const int base = ctx_bad ? 0 : span_base(ctx);    // first token of the attended span
   const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx - base,
                                     proportional ? slots_b : target_splits);
+  // Whatever the plan, the last 15% of a split's tokens take the default policy
+  // too: a mix of the two policies reads faster than either alone (32K step
+  // 87.7 -> 85.9 us, 8K 14.15 -> 13.78 us; 0.75 and 0.9 measure slower).
+  stream_tokens = min(stream_tokens, (int)(0.85f * (float)plan.split_tokens));
   // Row m of this (sequence, KV head) is query i = m / G of head h0 + m % G; its
   // flat index into q [B][Q][H_q][D], out and out_lse.  Query i sits at position
   // ctx - Q + i and attends to the tokens before it and itself.
