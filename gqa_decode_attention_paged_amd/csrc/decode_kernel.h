@@ -613,10 +613,10 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   constexpr int KCB = KIVI ? (CT >= BS ? CT / BS : 1) : 1;
   float kcs[KCB][8];
   // The tile loads' cache policy is an immediate, so each policy has its own
-  // copy of the loads, chosen per chunk by a wave-uniform branch.  Only the
-  // matrix path carries both copies: on the vector path the second copy costs
-  // 14-26 VGPRs, enough to halve some variants' occupancy, and it streams with
-  // the hint throughout.
+  // copy of the loads, chosen per chunk by a wave-uniform branch on the matrix
+  // path.  The vector path instead runs its chunk loop in two parts, one per
+  // policy: the branch costs it 14-26 VGPRs, enough to halve some variants'
+  // occupancy.
   using StreamPolicy = std::integral_constant<int, kStreamOnce>;
   using DefaultPolicy = std::integral_constant<int, 0>;
   auto issue_rows_with = [&](auto policy, int j, const char* pool, Vec (&r)[NI], float (&sc)[NI],
@@ -899,7 +899,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     // One chunk: partial dot products -> LDS; each lane sums and exponentiates its
     // own (token, row) scores; weights -> LDS; value sums.  SLOW handles the
     // split's tail chunk (V rows past the end are zeroed).
-    auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
+    auto run_chunk = [&](int j, auto slow_tag, auto next_tag, auto policy) {
       constexpr bool SLOW = decltype(slow_tag)::value;
       constexpr bool NEXT = decltype(next_tag)::value;     // chunk j+1 exists
       const int t0 = chunk_start(j);
@@ -959,7 +959,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
       if constexpr (NEXT) {
         advance_ids(j);
-        issue_rows(j + 1, kbase, kr, ks, true, true);
+        issue_rows_with(policy, j + 1, kbase, kr, ks, true, true);
       }
       __builtin_amdgcn_wave_barrier();
       // this lane's scores: token t = lane / M + q * TSTEP, row sg
@@ -1036,7 +1036,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep V(j+1) behind the value sums of chunk j
-      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs, false, false);
+      if constexpr (NEXT) issue_rows_with(policy, j + 1, vbase, vr, vs, false, false);
     };
 
     // Rotating pipeline: K(j+1) is issued right after the partial scores of chunk
@@ -1049,12 +1049,18 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     // Only a wave's last chunk can be partial, so the loop runs the fast path
     // only, and the last chunk is peeled, which also lets every loop iteration
     // issue the next loads unconditionally (K/V registers are reused in place).
-    for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
+    // The cache policy is an immediate of the load instructions, so the chunks
+    // whose successor streams with the hint and the rest run in two loops, one
+    // copy of the loads each (a per-chunk branch cost this path 14-26 VGPRs).
+    int j = 0;
+    for (; j + 1 < my_n && chunk_streams(j + 1); ++j)
+      run_chunk(j, std::false_type{}, std::true_type{}, StreamPolicy{});
+    for (; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{}, DefaultPolicy{});
     if (my_n > 0) {
       if (chunk_start(my_n - 1) + CT > s1)
-        run_chunk(my_n - 1, std::true_type{}, std::false_type{});
+        run_chunk(my_n - 1, std::true_type{}, std::false_type{}, StreamPolicy{});
       else
-        run_chunk(my_n - 1, std::false_type{}, std::false_type{});
+        run_chunk(my_n - 1, std::false_type{}, std::false_type{}, StreamPolicy{});
     }
 
     // Wave result: rows share m_ref, so value sums add without rescaling; l adds
