@@ -99,3 +99,35 @@ def test_copy_lists_must_pair_up():
     with pytest.raises(TypeError, match="src_blocks"):
         gqa.kv_copy_blocks(c["k_cache"], c["v_cache"], torch.zeros(3, dtype=torch.int64),
                            torch.zeros(3, dtype=torch.int32))
+
+
+def test_fused_step_rows_and_positions_are_checked():
+    c = _case()
+    k_new = torch.zeros((B, HKV, D), dtype=torch.bfloat16)
+    pos = torch.zeros(B, dtype=torch.int32)
+
+    def fused(**over):
+        a = {**c, "k_new": k_new, "v_new": k_new.clone(), "positions": pos, **over}
+        return gqa.paged_decode_append_attention(a["q"], a["k_new"], a["v_new"], a["positions"],
+                                                 a["k_cache"], a["v_cache"], a["block_tables"],
+                                                 a["context_lens"], 96)
+    with pytest.raises(ValueError, match="k_new"):
+        fused(k_new=torch.zeros((B, HKV + 1, D), dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="positions"):
+        fused(positions=pos.long())
+    with pytest.raises(ValueError, match="GPU memory"):
+        fused()
+
+
+def test_multi_position_outputs_are_checked():
+    c = _case()
+    Q = 3
+    q = torch.zeros((B, Q, HQ, D), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out:"):
+        gqa.paged_decode_multi_query(q, c["k_cache"], c["v_cache"], c["block_tables"],
+                                     c["context_lens"], 96,
+                                     out=torch.zeros((B, HQ, D), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out_lse"):
+        gqa.paged_decode_multi_query(q, c["k_cache"], c["v_cache"], c["block_tables"],
+                                     c["context_lens"], 96,
+                                     out_lse=torch.zeros((B, HQ), dtype=torch.float32))
