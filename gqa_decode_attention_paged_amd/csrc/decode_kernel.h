@@ -1118,7 +1118,10 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         O.x = fmaf(a, v.x, O.x); O.y = fmaf(a, v.y, O.y);
         O.z = fmaf(a, v.z, O.z); O.w = fmaf(a, v.w, O.w);
       }
-      const f32x4 o = O / L;
+      // A row may see none of this split's tokens (a query position before the
+      // split's start): its weight in the final merge is 2^-inf = 0, and its
+      // partial is 0 rather than 0/0, which would poison that merge.
+      const f32x4 o = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
       const float lse2 = any_bad ? __builtin_nanf("") : mx + log2f(L);
       if (nsplit == 1) {
         const float nan = __builtin_nanf("");
@@ -1146,7 +1149,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       L = fmaf(a, sm_l[w][g], L);
       O = fmaf(a, sm_acc(w, g, d), O);
     }
-    const float o = O / L;
+    const float o = L > 0.f ? O / L : 0.f;         // a row with no token here: 0, not 0/0
     const float lse2 = any_bad ? __builtin_nanf("") : mx + log2f(L);
     if (nsplit == 1) {
       p.out[row_index(g) * D + d] = any_bad ? __builtin_nanf("") : o;

@@ -222,3 +222,38 @@ def test_kivi_dtype_is_accepted(lib):
     assert call(k, None, 16) == 1
     assert call(k, 16, None) == 1
     assert lib.gqa_paged_decode_workspace_size(ctypes.byref(_shape(kv_dtype=3)), 1000) == 0
+
+
+def _split_plan(ctx, target=64):
+    """The split plan as the kernels apply it: at most `target` splits of a whole
+    number of 32-token chunks, none under 128 tokens unless the context is."""
+    if ctx <= 0:
+        return 0, 0
+    n = min(max((ctx + 127) // 128, 1), target)
+    st = -(-ctx // n)
+    st = -(-st // 32) * 32
+    return -(-ctx // st), st
+
+
+# Lengths at which the last split holds fewer tokens than query positions, so
+# that some query row (position ctx - Q + i) sees none of that split's tokens.
+SHORT_LAST_SPLIT = {2: (385, 513), 4: (385, 386, 513)}
+
+
+def test_split_mirror_matches_the_library(lib):
+    import gqa_decode_attention_paged_amd as gqa
+    for ctx in list(range(0, 3000)) + [8192, 32769]:
+        assert _split_plan(ctx)[0] == gqa.num_splits(ctx), ctx
+
+
+@pytest.mark.parametrize("nq", sorted(SHORT_LAST_SPLIT))
+def test_regression_lengths_give_a_row_no_token_of_the_last_split(lib, nq):
+    """The GPU regression for rows that see nothing of a split uses these lengths;
+    check that they really produce that case under the batch-invariant plan (and
+    under any target of at least 5 splits, the plan every small test batch gets)."""
+    for ctx in SHORT_LAST_SPLIT[nq]:
+        for target in (5, 8, 16, 64):
+            n, st = _split_plan(ctx, target)
+            last_start = (n - 1) * st
+            assert last_start > ctx - nq, (ctx, nq, target)   # query 0 sits at ctx - nq
+            assert last_start < ctx

@@ -75,6 +75,35 @@ def test_multi_query_ragged_on_four_wave_workgroups(gpu, hq, nq, dt):
     assert_parity(out, lse, ref, ref_lse, f"24 ragged sequences, G={hq // 8} Q={nq} {dt}")
 
 
+@pytest.mark.parametrize("batch_invariant", [False, True])
+@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 2, "bf16"), (32, 8, 4, "bf16"),
+                                          (8, 4, 2, "fp8"), (8, 4, 4, "fp8")])
+def test_rows_that_see_no_token_of_a_split(gpu, hq, hkv, nq, dt, batch_invariant):
+    """Regression: at 385, 386 and 513 tokens the last 128-token split holds fewer
+    tokens than the Q query positions, so some rows see none of its tokens; their
+    partial must weigh zero in the merge rather than turn the output into NaN.
+    Uniform batches of each length, then one ragged batch of all of them."""
+    batches = [[385] * 3, [386] * 3, [513] * 3, [385, 386, 513, 1000]]
+    for n, lens in enumerate(batches):
+        spec = small_spec(num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                          block_size=16, kv_dtype=dt, context=1000,
+                          case_id=6800 + 10 * n + hq + nq)
+        case = make_multi_query_case(spec, nq, seed=11, context_lens=lens,
+                                     append=(dt == "bf16"))
+        ref, ref_lse = _reference(case)
+        out, lse = _verify_step(gpu, case, to_device(case), batch_invariant=batch_invariant)
+        assert_parity(out, lse, ref, ref_lse, f"lens={lens} G={hq // hkv} Q={nq} {dt}")
+        if dt == "bf16":            # the fused verification step on the same lengths
+            d = to_device(case)
+            o2, l2 = gpu.paged_decode_multi_query_append(
+                d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["block_tables"],
+                d["context_lens"], max(lens), batch_invariant=batch_invariant)
+            torch.cuda.synchronize()
+            assert_parity(o2.cpu().numpy().astype(np.float64),
+                          l2.cpu().numpy().astype(np.float64), ref, ref_lse,
+                          f"fused, lens={lens} G={hq // hkv} Q={nq}")
+
+
 def test_single_position_matches_the_decode_entry_point_bitwise(gpu):
     spec = small_spec(num_seqs=3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                       context=2000, case_id=6100)
