@@ -559,10 +559,13 @@ gqa_status gqa_kv_copy_blocks(const gqa_paged_shape* s, void* k_cache, void* v_c
   p.v_scales = s->num_kv_heads * (kivi ? s->block_size : 1);
   p.block_bytes = (int64_t)s->num_kv_heads * s->block_size * s->head_dim * (fp8 ? 1 : 2);
   const int64_t slices = (p.block_bytes + gqa::kCopySliceBytes - 1) / gqa::kCopySliceBytes;
-  if ((int64_t)num_pairs * slices > INT32_MAX)
+  // One workgroup of kCopyThreads per work item, and a dispatch counts its grid in
+  // threads with 32 bits: at most UINT32_MAX / kCopyThreads (2^24 - 1) work items.
+  const int64_t max_items = (int64_t)UINT32_MAX / gqa::kCopyThreads;
+  if ((int64_t)num_pairs * slices > max_items)
     return fail(GQA_ERR_INVALID_ARG, "copy_blocks: %d pairs of %lld-byte blocks exceed one "
-                "launch (%lld 4 KiB slices, at most %d)", num_pairs, (long long)p.block_bytes,
-                (long long)num_pairs * slices, INT32_MAX);
+                "launch (%lld 4 KiB slices, at most %lld)", num_pairs, (long long)p.block_bytes,
+                (long long)num_pairs * slices, (long long)max_items);
   p.slices = (int32_t)slices;
   p.work_items = (uint32_t)(num_pairs * slices);
   st = launch(reinterpret_cast<const void*>(&gqa::kv_copy_blocks_kernel), dim3(p.work_items),

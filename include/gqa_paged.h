@@ -366,7 +366,8 @@ gqa_status gqa_kv_append_fp8(const gqa_paged_shape* shape, int32_t num_tokens,
  *   src_blocks, dst_blocks  [num_pairs] int32 device arrays; a pair with an id
  *                 outside [0, num_blocks), or with src == dst, copies nothing
  *   num_pairs     >= 0; one launch covers num_pairs x ceil(block bytes / 4 KiB)
- *                 work items, at most 2^31 - 1 (else GQA_ERR_INVALID_ARG)
+ *                 work items of 256 threads each, at most 2^24 - 1 of them (the
+ *                 dispatch's 32-bit thread count; else GQA_ERR_INVALID_ARG)
  * A source may appear in several pairs (a fork copies one block several times).
  * Performance only: pairs sharing a source are best listed next to each other,
  * as a fork produces them; the copies then read it through one XCD's L2.

@@ -192,10 +192,18 @@ def test_copy_blocks_validation(lib):
     f = _shape(kv_dtype=1)
     assert cb(ctypes.byref(f), P(16), P(16), None, None, P(16), P(16), 1, None) == 1
     assert cb(ctypes.byref(f), P(16), P(16), P(16), None, P(16), P(16), 1, None) == 1
-    # one launch covers pairs x 4 KiB slices: 2^23 pairs of 2 MiB blocks is 2^32 work items
+    # one launch covers pairs x 4 KiB slices of 256 threads each, and the dispatch
+    # counts threads in 32 bits: at most 2^24 - 1 work items
     big = _shape(num_kv_heads=256, num_q_heads=256, block_size=32)
     assert cb(ctypes.byref(big), P(16), P(16), None, None, P(16), P(16), 1 << 23, None) == 1
     assert "exceed one launch" in lib.gqa_last_error().decode()
+    one = _shape(num_kv_heads=1, num_q_heads=1, head_dim=128, block_size=16)   # 4 KiB blocks
+    assert cb(ctypes.byref(one), P(16), P(16), None, None, P(16), P(16), 1 << 24, None) == 1
+    assert "exceed one launch" in lib.gqa_last_error().decode()
+    if not os.path.exists("/dev/kfd"):
+        # no GPU: one item fewer passes validation and fails only at the launch
+        assert cb(ctypes.byref(one), P(16), P(16), None, None, P(16), P(16), (1 << 24) - 1,
+                  None) == 4
 
 
 def test_append_fp8_validation(lib):
