@@ -24,6 +24,8 @@ __all__ = [
     "load", "GqaError", "PagedShape", "kv_append", "paged_decode_attention",
     "workspace_size", "num_splits", "kv_gather", "last_error", "version", "LIB_PATH",
     "paged_decode_append_attention", "make_workspace", "workspace_init", "make_shape",
+    "workspace_status", "STATUS_BAD_CONTEXT_LEN", "STATUS_CONTEXT_OVER_HINT",
+    "STATUS_BAD_BLOCK_ID", "STATUS_BAD_APPEND",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_paged.so")
@@ -32,6 +34,11 @@ GQA_KV_BF16 = 0
 GQA_KV_FP8_E4M3 = 1
 GQA_KV_FP8_E4M3_KIVI = 2
 GQA_FLAG_BATCH_INVARIANT = 1
+# Device status bits recorded in a workspace by the attention calls (gqa_paged.h).
+STATUS_BAD_CONTEXT_LEN = 1
+STATUS_CONTEXT_OVER_HINT = 2
+STATUS_BAD_BLOCK_ID = 4
+STATUS_BAD_APPEND = 8
 STATUS_NAMES = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
                 3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_HIP"}
 
@@ -94,6 +101,9 @@ def load():
     lib.gqa_paged_decode_workspace_init.restype = ctypes.c_int
     lib.gqa_kv_append_fp8.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.gqa_kv_append_fp8.restype = ctypes.c_int
+    lib.gqa_workspace_read_status.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_uint32), _P]
+    lib.gqa_workspace_read_status.restype = ctypes.c_int
     lib.gqa_kv_copy_blocks.argtypes = [S, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
     lib.gqa_kv_copy_blocks.restype = ctypes.c_int
     lib.gqa_kv_gather.argtypes = [S, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P]
@@ -419,6 +429,19 @@ def workspace_init(shape: PagedShape, max_context_len: int, workspace):
     _check(load().gqa_paged_decode_workspace_init(
         ctypes.byref(shape), int(max_context_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(workspace)))
+
+
+def workspace_status(workspace, clear=False) -> int:
+    """The STATUS_* bits the attention calls recorded in this workspace (blocking:
+    waits for the current stream); ``clear`` zeroes them afterwards."""
+    chk = _Checks()
+    chk(workspace, "workspace")
+    chk.on_gpu()
+    word = ctypes.c_uint32(0)
+    _check(load().gqa_workspace_read_status(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), 1 if clear else 0,
+        ctypes.byref(word), _stream(workspace)))
+    return int(word.value)
 
 
 def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,

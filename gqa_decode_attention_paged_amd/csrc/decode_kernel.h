@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gqa_paged.h"
 
 namespace gqa {
 
@@ -80,6 +81,7 @@ struct DecodeParams {
   float* ws_o;                  // [B][Hkv][max_splits][M][D] partial outputs (normalised)
   float* ws_lse;                // [B][Hkv][max_splits][M]    partial base-2 lse
   uint32_t* counters;           // [B][Hkv] arrivals, kCounterStride words apart; zero between calls
+  uint32_t* status;             // sticky GQA_STATUS_* bits (a word in the first counter's line)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;                // G = num_q_heads / num_kv_heads (a power of two)
@@ -150,6 +152,12 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 // s_waitcnt vmcnt(0): every vector memory access of this wave (stores included) done.
 __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Record a bad device-resident input in the workspace's status word (a vector
+// atomic OR, issued by one lane; the bits stay set until the host clears them).
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
+  __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicySc1 = 16;         // buffer instruction cache-policy bit "sc1"
@@ -188,9 +196,12 @@ __device__ __forceinline__ void append_rows(const DecodeParams& p, const int32_t
                                             int max_blocks, int b, int kvh, int pos, int D,
                                             int BS) {
   const int units = D / 8;
-  if ((int)threadIdx.x >= units || pos < 0 || pos >= max_blocks * BS) return;
-  const int blk = block_tables[(size_t)b * max_blocks + pos / BS];
-  if (blk < 0 || blk >= p.num_blocks) return;
+  if ((int)threadIdx.x >= units || pos < 0) return;
+  const int blk = pos < max_blocks * BS ? block_tables[(size_t)b * max_blocks + pos / BS] : -1;
+  if (blk < 0 || blk >= p.num_blocks) {            // past the table, or not a block of the pool
+    if (threadIdx.x == 0) raise_status(p.status, GQA_STATUS_BAD_APPEND);
+    return;
+  }
   const size_t src = ((size_t)b * p.num_kv_heads + kvh) * D + threadIdx.x * 8;
   const size_t dst = (((size_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * D + threadIdx.x * 8;
   *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + dst) =
@@ -472,10 +483,12 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   };
   if (p.positions && split == owner && !pos_in_split) {
     if constexpr (FP8) {
-      if (wave == 0 && pos >= 0 && pos < max_blocks * BS) {
-        const int blk = block_tables[(size_t)b * max_blocks + pos / BS];
+      if (wave == 0 && pos >= 0) {
+        const int blk = pos < max_blocks * BS ? block_tables[(size_t)b * max_blocks + pos / BS] : -1;
         if ((unsigned)blk < (unsigned)p.num_blocks)
           append_fp8_tile(blk, pos % BS, 1, ((size_t)b * p.num_kv_heads + kvh) * D, 0);
+        else if (lane == 0)
+          raise_status(p.status, GQA_STATUS_BAD_APPEND);
       }
     } else {
       append_rows(p, block_tables, max_blocks, b, kvh, pos, D, BS);
@@ -485,6 +498,8 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   if (degenerate) {
     if (split != 0) return;
     const bool bad = ctx_bad || too_long;
+    if (tid == 0 && bad)
+      raise_status(p.status, ctx_bad ? GQA_STATUS_BAD_CONTEXT_LEN : GQA_STATUS_CONTEXT_OVER_HINT);
     const float v = bad ? __builtin_nanf("") : 0.f;
     for (int i = tid; i < R * D; i += NT) p.out[row_index(i / D) * D + i % D] = v;
     if (p.out_lse && tid < R) p.out_lse[row_index(tid)] = bad ? __builtin_nanf("") : kNegInf;
@@ -519,7 +534,10 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       const int hi = k == 0 ? min(a0 + na, nxt) : a0 + na;
       if (na <= 0 || lo >= hi || lo < s0 || lo >= s1) continue;
       const int blk = bt[lo / BS];
-      if ((unsigned)blk >= (unsigned)p.num_blocks) continue;
+      if ((unsigned)blk >= (unsigned)p.num_blocks) {
+        if (tid == 0) raise_status(p.status, GQA_STATUS_BAD_APPEND);
+        continue;
+      }
       any_here = true;
       if (((lo - s0) / CT) % WAVES != wave) continue;
       const size_t row = (((size_t)b * rows_per_seq + (lo - a0)) * p.num_kv_heads + kvh) * D;
@@ -551,6 +569,8 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
             *reinterpret_cast<const uint4*>(p.k_new + src);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + dst) =
             *reinterpret_cast<const uint4*>(p.v_new + src);
+      } else if (lane == 0) {
+        raise_status(p.status, GQA_STATUS_BAD_APPEND);
       }
     }
     if (wrote) wait_vector_memory();
@@ -1095,6 +1115,7 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   int any_bad = 0;
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) any_bad |= sm_flag[w];
+  if (any_bad && tid == 0) raise_status(p.status, GQA_STATUS_BAD_BLOCK_ID);
   const size_t prow = ((size_t)b * p.num_kv_heads + kvh) * p.max_splits;   // partial rows
   if constexpr (M * D >= 4 * NT) {
     // Four or more elements per thread: four consecutive dims at a time, and

@@ -430,6 +430,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
   p.ws_lse = reinterpret_cast<float*>(ws + wl.lse_off);
   p.counters = reinterpret_cast<uint32_t*>(ws);
+  p.status = reinterpret_cast<uint32_t*>(ws + GQA_WORKSPACE_STATUS_OFFSET);
   p.num_q_heads = s->num_q_heads;
   p.num_kv_heads = s->num_kv_heads;
   p.group = G;
@@ -527,6 +528,31 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* s, int32_t max
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&gqa::zero_words_kernel),
                                  dim3(blocks), dim3(256), argv, 0, stream);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "workspace init failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gqa_status gqa_workspace_read_status(const void* workspace, size_t workspace_bytes, int32_t clear,
+                                     uint32_t* status, hipStream_t stream) {
+  if (!workspace || !status)
+    return fail(GQA_ERR_INVALID_ARG, "read_status: NULL workspace or status");
+  if (workspace_bytes < GQA_WORKSPACE_STATUS_OFFSET + sizeof(uint32_t))
+    return fail(GQA_ERR_WORKSPACE, "read_status: workspace of %zu bytes holds no status word",
+                workspace_bytes);
+  uint32_t* word = reinterpret_cast<uint32_t*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                               GQA_WORKSPACE_STATUS_OFFSET);
+  uint32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, word, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "read_status: %s", hipGetErrorString(e));
+  *status = host;
+  if (clear && host != 0) {
+    size_t n = 1;
+    void* argv[] = {&word, &n};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&gqa::zero_words_kernel), dim3(1), dim3(64),
+                        argv, 0, stream);
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "read_status: clear failed: %s",
+                                     hipGetErrorString(e));
+  }
   return ok();
 }
 

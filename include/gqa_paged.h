@@ -58,7 +58,10 @@
  *    context lengths) are checked inside the kernels: a sequence whose context
  *    length or attended block ids are out of range gets NaN in every output
  *    element and lse of its heads (nothing outside the buffers is read), and an
- *    append whose position or block id is out of range writes nothing.
+ *    append whose position or block id is out of range writes nothing.  The
+ *    attention calls also record each such fault as a GQA_STATUS_* bit in the
+ *    workspace's status word, which gqa_workspace_read_status returns, so the
+ *    host can tell a corrupted table or length from NaN data.
  */
 #ifndef GQA_PAGED_H
 #define GQA_PAGED_H
@@ -103,6 +106,24 @@ enum {
    * never depend on the order of the sequences. */
   GQA_FLAG_BATCH_INVARIANT = 1
 };
+
+/* Device status bits.  The attention calls (all of which take a workspace) OR
+ * these into the 32-bit word at byte GQA_WORKSPACE_STATUS_OFFSET of their
+ * workspace when they meet a bad device-resident input.  The bits are sticky:
+ * no call clears them; gqa_workspace_read_status (clear = 1) or
+ * gqa_paged_decode_workspace_init does.  The table and length contract they
+ * check is that of *Module 10*, "Mapping logical positions to physical
+ * blocks", and *The Mathematics of Transformer Inference* §9: every logical
+ * block a sequence attends maps to a physical block of the pool. */
+enum {
+  GQA_STATUS_BAD_CONTEXT_LEN = 1,   /* context_lens[b] < 0, beyond max_blocks_per_seq *
+                                       block_size, or 0 < context_lens[b] < num_queries  */
+  GQA_STATUS_CONTEXT_OVER_HINT = 2, /* context_lens[b] > max_context_len (the launch hint) */
+  GQA_STATUS_BAD_BLOCK_ID = 4,      /* an attended table entry outside [0, num_blocks)    */
+  GQA_STATUS_BAD_APPEND = 8         /* a fused append's position is past the table, or its
+                                       table entry is not a block of the pool            */
+};
+#define GQA_WORKSPACE_STATUS_OFFSET 4
 
 /* Host-side description of one paged KV cache and one batch of sequences. */
 typedef struct gqa_paged_shape {
@@ -190,11 +211,14 @@ size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max
  *                 gqa_paged_decode_workspace_size(shape, max_context_len) bytes,
  *                 16-byte aligned.  It starts with one arrival counter (u32) per
  *                 (sequence, KV head), 256 bytes apart, followed by the partial
- *                 results of the context splits.  The first B*H_kv*64 words
- *                 (B*H_kv*256 bytes) must be zero before a
+ *                 results of the context splits; the word at byte
+ *                 GQA_WORKSPACE_STATUS_OFFSET (in the first counter's 256 bytes) is
+ *                 the status word.  The first B*H_kv*64 words
+ *                 (B*H_kv*256 bytes) must be zero before the first
  *                 call (gqa_paged_decode_workspace_init, or any zero fill); every
- *                 call leaves them zero again, so a workspace prepared once serves
- *                 any later call with no more (sequence, KV head) pairs.  One
+ *                 call leaves the counters zero again, so a workspace prepared once
+ *                 serves any later call with no more (sequence, KV head) pairs (the
+ *                 status word keeps its bits until cleared).  One
  *                 workspace serves one call at a time: calls sharing it must be
  *                 ordered on one stream.
  * Inputs are read only.  One kernel runs on `stream`: each workgroup attends
@@ -311,13 +335,30 @@ gqa_status gqa_paged_decode_append_attention(const gqa_paged_shape* shape,
 
 /*
  * gqa_paged_decode_workspace_init — zero the arrival counters (the first
- * B*H_kv*64 words) of a workspace; workspace_bytes must cover them.  Enqueued on
+ * B*H_kv*64 words, the status word among them) of a workspace; workspace_bytes
+ * must cover them.  Enqueued on
  * `stream` as a small fill kernel (no memset), so it may be captured in a HIP
  * graph.  max_context_len is validated but does not change what is zeroed.
  */
 gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t max_context_len,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
+
+/*
+ * gqa_workspace_read_status — the GQA_STATUS_* bits that the attention calls
+ * enqueued so far on `stream` have recorded in this workspace (0: none met a bad
+ * device-resident input).  Blocking: copies the word to the host after the
+ * stream's earlier work and waits for the stream.  clear != 0 then enqueues a
+ * zero fill of the word on `stream` (a small kernel, no memset).
+ *   workspace, workspace_bytes  a workspace of the attention calls (device)
+ *   status        host pointer receiving the bits
+ * Returns GQA_ERR_INVALID_ARG for NULL pointers, GQA_ERR_WORKSPACE when
+ * workspace_bytes does not reach the word, GQA_ERR_HIP when the copy fails.
+ * Cites: *Module 10*, "Mapping logical positions to physical blocks"; *The
+ * Mathematics of Transformer Inference* §9 (the table contract checked).
+ */
+gqa_status gqa_workspace_read_status(const void* workspace, size_t workspace_bytes,
+                                     int32_t clear, uint32_t* status, hipStream_t stream);
 
 /*
  * gqa_kv_append_fp8 — append num_tokens (T) new tokens per sequence to an fp8
