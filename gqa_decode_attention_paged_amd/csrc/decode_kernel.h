@@ -1211,12 +1211,15 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   // threads, else kMergeBatch per round
   constexpr int MB = (kMaxSplits + SP - 1) / SP < kMergeBatch ? (kMaxSplits + SP - 1) / SP
                                                                 : kMergeBatch;
+  // Only splits that exist are loaded: each load is a coherent read from memory
+  // through this one compute unit, and MB covers the largest split count.
   auto load_batch = [&](int c, int sb, f32x4 (&v)[MB]) {
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
       const int si = sb + u * SP;
-      v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                 src, (si < nsplit ? si * C4 + c : 0) * 16, 0, kCachePolicySc1));
+      v[u] = si < nsplit ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               src, (si * C4 + c) * 16, 0, kCachePolicySc1))
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   f32x4 v[MB];
