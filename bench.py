@@ -1,7 +1,12 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark: KV-read GB/s (vs MI355X peak HBM bandwidth) and us/step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+    python bench.py --probe            # the read-bandwidth ceilings (stream and paged gather)
+
+The default workload is the 32K long-context step (B=4, 64 query / 8 KV heads,
+d_h 128, 32768 cached tokens + 1 appended per sequence, block 32, bf16), the
+largest configuration that fits one GPU.
 
 One step = one pass of the decode hot path over one batch: the KV append of the
 new token (for workloads that append) and paged decode attention, split over
@@ -32,8 +37,12 @@ the destination blocks written.
 
 Prints one JSON line (rank 0, N=1).  `value` = algorithmic KV bytes per step /
 step time.  `roofline.achieved` = the same bytes / the decode-attention call's
-average duration measured with HIP events on the launch stream.  The float64
-CPU oracle is timed on a bounded sample as `cpu_baseline`.
+average duration measured with HIP events on the launch stream;
+`roofline.sustained_gbs` is what a read probe with the same tiles, table and
+bytes per launch reaches on the same box (no compute), and `distribution` the
+p10/p50/p90 of the per-step kernel time over further graph replays.  The float64
+CPU oracle is timed on a bounded sample as `cpu_baseline`; `context` quotes the
+pages' own figures for other hardware.
 """
 import argparse
 import hashlib
@@ -50,6 +59,38 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 ROTATE_BYTES = 1 << 30         # distance between reuses of one pool copy
 COPY_BYTES = 256 << 20         # read and written by the PMC calibration kernel
 METRIC = "decode-attention KV-read HBM GB/s (% of MI355X peak) and µs/step"
+DEFAULT_WORKLOAD = "long"
+
+# Figures the pages quote for other hardware: context only, neither target nor
+# baseline (the metric's denominator is MI355X's own peak).
+PAGES_CONTEXT = {
+    "note": "the pages' own figures for other hardware; context only",
+    "h100_sxm": {"bf16_dense_tflops": 989.0, "hbm_tb_per_s": 3.35,
+                 "source": "Module 10: Inference and Deployment Serving, matrix-vector "
+                           "section (ridge 989/3.35 = 295 FLOP/byte); The Mathematics of "
+                           "Transformer Inference, section 3"},
+    "tpu_v5e": {"bf16_tflops": 197.0, "hbm_tb_per_s": 0.82,
+                "source": "The Mathematics of Transformer Inference, section 3"},
+    "cpu_4_threads": {"effective_gb_per_s": 48.24,
+                      "workload": "float32 8192 x 8192 matrix-vector product, B = 1, "
+                                  "5.566 ms per product",
+                      "source": "Module 10: Inference and Deployment Serving, 'Measure "
+                                "the CPU, don't guess from the clock' (Lab 1)"},
+}
+
+
+def pages_context(kv_bytes):
+    """PAGES_CONTEXT plus the time each quoted device would need to read this step's KV
+    bytes once at its quoted bandwidth (the decode-step lower bound of The Mathematics
+    of Transformer Inference, section 6)."""
+    ctx = json.loads(json.dumps(PAGES_CONTEXT))
+    ctx["kv_read_us_at_quoted_bandwidth"] = {
+        "h100_sxm": round(kv_bytes / 3.35e12 * 1e6, 2),
+        "tpu_v5e": round(kv_bytes / 0.82e12 * 1e6, 2),
+        "cpu_4_threads": round(kv_bytes / 48.24e9 * 1e6, 2),
+        "mi355x_peak": round(kv_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
+    }
+    return ctx
 
 
 def kv_bytes_per_step(spec, context_lens):
@@ -113,13 +154,66 @@ def identity_layout(case):
     case["block_tables"] = ident
 
 
+KERNEL_SOURCES = ("common.h", "decode_kernel.h", "gqa_paged.hip", "kv_cache_ops.h")
+
+
 def kernel_source_hash():
+    """Hash of the sources the decode and block-copy kernels are built from (their
+    launch code included); the probes' sources are not part of it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gqa_decode_attention_paged_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def profiled_kernel_time(workload):
+    """Per-dispatch duration statistics of the workload's kernel from a committed
+    rocprofv3 kernel trace (profiles/kernel_time_<workload>.json), if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"kernel_time_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t
+
+
+def write_kernel_time(workload, trace_dir, kv_bytes):
+    """Host only: per-dispatch durations of the workload's kernel from a rocprofv3
+    `--kernel-trace -f csv` output directory -> profiles/kernel_time_<workload>.json."""
+    import csv
+    import glob
+    import statistics
+    kname = "kv_copy_blocks_kernel" if workload == "cow_fork" else "paged_decode_kernel"
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    durs = []
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if kname in row["Kernel_Name"]:
+                    durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    if not durs:
+        raise SystemExit(f"no {kname} dispatches in {files}")
+    durs.sort()
+    q = lambda f: durs[min(len(durs) - 1, int(f * len(durs)))]
+    out = {"workload": workload, "kernel": kname, "kernel_source_sha": kernel_source_hash(),
+           "dispatches": len(durs), "avg_us": round(statistics.fmean(durs), 3),
+           "p10_us": round(q(0.1), 3), "p50_us": round(statistics.median(durs), 3),
+           "p90_us": round(q(0.9), 3), "min_us": round(durs[0], 3), "max_us": round(durs[-1], 3),
+           "algorithmic_bytes_per_call": kv_bytes}
+    out["achieved_gbs_avg"] = round(kv_bytes / (out["avg_us"] * 1e-6) / 1e9, 2)
+    out["frac_avg"] = round(out["achieved_gbs_avg"] / PEAK_HBM_GBS, 4)
+    path = os.path.join(ROOT, "profiles", f"kernel_time_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def counted_traffic(workload):
@@ -226,7 +320,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama8b",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4",
                              "mha_fp8_append", "mha_fp8_kivi", "cow_fork"])
     ap.add_argument("--seed", type=int, default=0)
@@ -242,6 +336,24 @@ def main():
     ap.add_argument("--traffic-from", metavar="PMC_DIR",
                     help="host only: write profiles/traffic_<workload>.json from rocprofv3 "
                          "PMC runs stored under PMC_DIR/{fetch,write,copy_fetch,copy_write}")
+    ap.add_argument("--kernel-stats-from", metavar="TRACE_DIR",
+                    help="host only: write profiles/kernel_time_<workload>.json from a "
+                         "rocprofv3 --kernel-trace -f csv run of this workload")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed replays of the K-step graph, for at least this long, right "
+                         "before the timed pass: the GPU's clocks settle over the first "
+                         "10-20 ms of sustained work, and a pass inside that transient runs "
+                         "about 3%% slow")
+    ap.add_argument("--reps", type=int, default=10,
+                    help="further timed replays of the K-step graph for the p10/p50/p90 "
+                         "distribution (outside the headline timing)")
+    ap.add_argument("--batch-invariant", action="store_true",
+                    help="split every sequence by its own length only (GQA_FLAG_BATCH_INVARIANT)")
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip the read probe of the workload's tile pattern")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the read-bandwidth probes (plain streaming read, paged "
+                         "gather at each tile size, a lone workgroup) and print their rates")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -264,6 +376,15 @@ def main():
         write_traffic(args.workload, args.traffic_from,
                       kv_bytes_per_step(spec, make_case(spec, seed=args.seed)["context_lens"]))
         return
+    if args.kernel_stats_from:
+        from workloads import make_case, SPECS
+        if args.workload == "cow_fork":
+            kvb = fork_geometry()[5]
+        else:
+            spec = SPECS[base_name]
+            kvb = kv_bytes_per_step(spec, make_case(spec, seed=args.seed)["context_lens"])
+        write_kernel_time(args.workload, args.kernel_stats_from, kvb)
+        return
 
     import torch
 
@@ -282,6 +403,10 @@ def main():
         return
 
     gqa.load()
+    if args.probe:
+        for line in probe_suite(args, np, torch, gqa):
+            print(json.dumps(line), flush=True)
+        return
     if args.workload == "cow_fork":
         print(json.dumps(bench_block_copy(args, np, torch, gqa)), flush=True)
         return
@@ -320,7 +445,8 @@ def main():
         k8_new, v8_new = bf16(case["fp8_k_new"][:, 0]), bf16(case["fp8_v_new"][:, 0])
         start8 = torch.from_numpy(case["fp8_start"]).to(dev)
     max_ctx = int(case["context_lens"].max())
-    shape = gqa.make_shape(spec.num_seqs, spec.num_q_heads, k0, bt)
+    inv = args.batch_invariant
+    shape = gqa.make_shape(spec.num_seqs, spec.num_q_heads, k0, bt, batch_invariant=inv)
     ws = torch.zeros(max(16, gqa.multi_query_workspace_size(shape, nq, max_ctx)),
                      dtype=torch.uint8, device=dev)
     rows = (spec.num_seqs, nq, spec.num_q_heads) if verify else (spec.num_seqs, spec.num_q_heads)
@@ -334,19 +460,35 @@ def main():
             ksc, vsc = scales[i % copies]
             gqa.paged_decode_append_attention(q, k8_new, v8_new, start8, kc, vc, bt, ctx,
                                               max_ctx, scale, out=out, out_lse=lse,
-                                              workspace=ws, k_scale=ksc, v_scale=vsc)
+                                              workspace=ws, k_scale=ksc, v_scale=vsc,
+                                              batch_invariant=inv)
         elif verify:               # fused: commit the 4 new tokens, attend for all 4 positions
             gqa.paged_decode_multi_query_append(q, k_new, v_new, kc, vc, bt, ctx, max_ctx, scale,
-                                                out=out, out_lse=lse, workspace=ws)
+                                                out=out, out_lse=lse, workspace=ws,
+                                                batch_invariant=inv)
         elif k_new is not None:    # fused: commit the new token and attend, one kernel
             gqa.paged_decode_append_attention(q, k_new, v_new, pos, kc, vc, bt, ctx, max_ctx,
-                                              scale, out=out, out_lse=lse, workspace=ws)
+                                              scale, out=out, out_lse=lse, workspace=ws,
+                                              batch_invariant=inv)
         else:
             gqa.paged_decode_attention(q, kc, vc, bt, ctx, max_ctx, scale, ks, vs, out=out,
-                                       out_lse=lse, workspace=ws)
+                                       out_lse=lse, workspace=ws, batch_invariant=inv)
 
-    ms_per_step, call_ms, graphed = _timed(torch, args, step)
+    ms_per_step, call_ms, graphed, dist = _timed(torch, args, step)
+    if gqa.workspace_status(ws) != 0:
+        raise SystemExit(f"device status {gqa.workspace_status(ws)}: bad inputs in the bench")
     achieved = kv_bytes / (call_ms * 1e-3) / 1e9
+    esz = 1 if spec.kv_dtype.startswith("fp8") else 2
+    del pools
+    if fp8_append:
+        del scales
+    torch.cuda.empty_cache()
+    sustained = None
+    if not args.no_sustained:
+        nb = (case["context_lens"].astype(np.int64) + spec.block_size - 1) // spec.block_size
+        sustained = sustained_probe(args, np, torch, gqa,
+                                    tile_bytes=spec.block_size * spec.head_dim * esz,
+                                    num_tiles=int(nb.sum()) * spec.num_kv_heads * 2)
     if fp8_append:
         kernel = ("paged_decode_kernel (fused fp8 KV append with the power-of-two scale "
                   "policy + split attention + log-sum-exp merge)")
@@ -361,6 +503,7 @@ def main():
     else:
         kernel = "paged_decode_kernel (split attention + log-sum-exp merge)"
 
+    prof = profiled_kernel_time(args.workload) if not (args.identity_table or inv) else None
     result = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -384,7 +527,9 @@ def main():
             "query_positions": nq, "fp8_append": fp8_append,
             "block_table": "identity (control run)" if args.identity_table else "random permutation",
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
+            "split_policy": "batch-invariant" if inv else "default (fills the GPU once)",
         },
+        "distribution": dist,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -397,7 +542,14 @@ def main():
             "timing": ("HIP events on the launch stream around one replay of a graph of the "
                        "K steps (one kernel per step), divided by K" if graphed else
                        "HIP events around K eager steps, divided by K"),
+            "sustained_gbs": sustained["gbs"] if sustained else None,
+            "frac_of_sustained": (round(achieved / sustained["gbs"], 4) if sustained else None),
+            "sustained_probe": sustained["what"] if sustained else None,
+            "rocprof": ({k: prof[k] for k in ("dispatches", "avg_us", "p10_us", "p50_us",
+                                              "p90_us", "achieved_gbs_avg", "frac_avg")}
+                        if prof else None),
         },
+        "context": pages_context(kv_bytes),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, kv_bytes, args.cpu_seconds)
@@ -410,7 +562,10 @@ def main():
 
 def _timed(torch, args, step):
     """Warm up, record the K timed steps into a HIP graph (unless --no-graph), and
-    return (wall ms per step, event ms per step on the launch stream, graph used)."""
+    return (wall ms per step, event ms per step on the launch stream, graph used,
+    distribution).  The headline figures come from exactly one timed pass of the K
+    steps; the distribution (p10/p50/p90 of the per-step event time) from args.reps
+    further passes, each timed alone."""
     dev = torch.device("cuda:0")
     for i in range(args.warmup):
         step(i)
@@ -427,6 +582,14 @@ def _timed(torch, args, step):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+    settle_until = time.perf_counter() + getattr(args, "settle_ms", 0.0) * 1e-3
+    while time.perf_counter() < settle_until:       # untimed: lets the clocks settle
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(args.warmup + i)
+        torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -439,7 +602,102 @@ def _timed(torch, args, step):
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e3 / args.steps, start.elapsed_time(stop) / args.steps, graph is not None
+    per_step = []
+    for r in range(args.reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(args.warmup + (r + 1) * args.steps + i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_step.append(a.elapsed_time(b) * 1e3 / args.steps)
+    dist = None
+    if per_step:
+        srt = sorted(per_step)
+        pick = lambda f: round(srt[min(len(srt) - 1, int(f * len(srt)))], 3)
+        dist = {"reps": len(per_step), "steps_per_rep": args.steps,
+                "unit": "µs per step (HIP events per pass of the K steps)",
+                "p10": pick(0.1), "p50": round(sorted(per_step)[len(srt) // 2], 3),
+                "p90": pick(0.9)}
+    return (wall * 1e3 / args.steps, start.elapsed_time(stop) / args.steps, graph is not None,
+            dist)
+
+
+def probe_rate(args, np, torch, gqa, *, total_bytes, tile_bytes, table, non_temporal,
+               workgroups=None, steps=None):
+    """One read-probe configuration: a graph of `steps` launches, each reading
+    total_bytes in tiles of tile_bytes (through a random permutation table, or as a
+    plain stream), rotated over copies so each launch reads bytes last touched at
+    least 1 GiB of reads ago.  Returns a dict with GB/s (events) and its spread."""
+    dev = torch.device("cuda:0")
+    if workgroups is None:
+        workgroups = torch.cuda.get_device_properties(dev).multi_processor_count
+    ntiles = total_bytes // tile_bytes
+    copies = max(1, math.ceil(ROTATE_BYTES / (ntiles * tile_bytes)) + 1)
+    buf = torch.zeros(copies * ntiles * tile_bytes, dtype=torch.uint8, device=dev)
+    ids = None
+    if table:
+        perm = np.random.default_rng([args.seed, tile_bytes, ntiles]).permutation(ntiles)
+        ids = torch.from_numpy(perm.astype(np.int32)).to(dev)
+    sink = torch.empty(workgroups * 8, dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+
+    def step(i):
+        gqa.probe_read(base + (i % copies) * ntiles * tile_bytes, ntiles, ids, ntiles,
+                       tile_bytes, non_temporal, workgroups, sink)
+
+    sub = argparse.Namespace(**vars(args))
+    sub.steps = steps or max(args.steps, 20)
+    sub.warmup = max(args.warmup, 3)
+    sub.reps = max(args.reps, 5)
+    sub.no_graph = False
+    _, call_ms, _, dist = _timed(torch, sub, step)
+    del buf
+    torch.cuda.empty_cache()
+    gbs = lambda us: round(ntiles * tile_bytes / (us * 1e-6) / 1e9, 1)
+    return {"gbs": gbs(call_ms * 1e3), "us_per_launch": round(call_ms * 1e3, 3),
+            "gbs_p10_p50_p90": [gbs(dist["p90"]), gbs(dist["p50"]), gbs(dist["p10"])],
+            "bytes_per_launch": ntiles * tile_bytes, "tile_bytes": tile_bytes,
+            "table": "random permutation" if table else "none (contiguous stream)",
+            "non_temporal": bool(non_temporal), "workgroups": workgroups,
+            "launches": sub.steps, "copies_rotated": copies}
+
+
+def sustained_probe(args, np, torch, gqa, tile_bytes, num_tiles):
+    """The read probe with the workload's own pattern: its (block, KV head) tile size,
+    as many tiles per launch as the step reads (K and V), a random table, and the
+    non-temporal hint of the decode kernel's tile loads."""
+    r = probe_rate(args, np, torch, gqa, total_bytes=num_tiles * tile_bytes,
+                   tile_bytes=tile_bytes, table=True, non_temporal=1)
+    r["what"] = (f"gqa_probe_read: {num_tiles} random {tile_bytes}-byte tiles per launch "
+                 f"({r['bytes_per_launch']} bytes), non-temporal loads, {r['workgroups']} "
+                 f"8-wave workgroups, no compute; HIP events over {r['launches']} launches")
+    return r
+
+
+def probe_suite(args, np, torch, gqa):
+    """The read-bandwidth ceilings: a plain streaming read at several sizes, the paged
+    gather at each tile size the pools use, and one workgroup gathering alone, each
+    with the non-temporal hint and with the default policy."""
+    runs = []
+    for size in (32 << 20, 128 << 20, 512 << 20):
+        for nt in (1, 0):
+            runs.append(dict(total_bytes=size, tile_bytes=16384, table=False, non_temporal=nt))
+    for tile in (2048, 4096, 8192, 16384):
+        for nt in (1, 0):
+            runs.append(dict(total_bytes=512 << 20, tile_bytes=tile, table=True, non_temporal=nt))
+    for nt in (1, 0):
+        runs.append(dict(total_bytes=8 << 20, tile_bytes=4096, table=True, non_temporal=nt,
+                         workgroups=1, steps=5))
+    out = []
+    for kw in runs:
+        r = probe_rate(args, np, torch, gqa, **kw)
+        r["frac_of_peak"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+        out.append(r)
+    return out
 
 
 def bench_block_copy(args, np, torch, gqa):
@@ -460,7 +718,7 @@ def bench_block_copy(args, np, torch, gqa):
         src, dst = lists[i % copies]
         gqa.kv_copy_blocks(k, v, src, dst)
 
-    ms_per_step, call_ms, graphed = _timed(torch, args, step)
+    ms_per_step, call_ms, graphed, dist = _timed(torch, args, step)
     achieved = alg_bytes / (call_ms * 1e-3) / 1e9
     result = {
         "metric": "copy-on-write block copy HBM GB/s (unique source blocks read + copies "
@@ -476,6 +734,7 @@ def bench_block_copy(args, np, torch, gqa):
             "copies_per_step": pairs, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
             "kv_dtype": "bf16", "bytes_per_step": alg_bytes, "pool_ranges_rotated": copies,
         },
+        "distribution": dist,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),

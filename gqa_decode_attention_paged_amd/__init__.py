@@ -101,6 +101,9 @@ def load():
     lib.gqa_paged_decode_workspace_init.restype = ctypes.c_int
     lib.gqa_kv_append_fp8.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.gqa_kv_append_fp8.restype = ctypes.c_int
+    lib.gqa_probe_read.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.gqa_probe_read.restype = ctypes.c_int
     lib.gqa_workspace_read_status.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_uint32), _P]
     lib.gqa_workspace_read_status.restype = ctypes.c_int
@@ -480,6 +483,24 @@ def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_sca
                                      _ptr(k_scale), _ptr(v_scale), _ptr(src_blocks),
                                      _ptr(dst_blocks), int(src_blocks.numel()),
                                      _stream(k_cache)))
+
+
+def probe_read(pool_address, pool_tiles, tile_ids, num_tiles, tile_bytes, non_temporal,
+               num_workgroups, sink):
+    """One read-probe launch (measurement only): num_tiles tiles of tile_bytes bytes from
+    the device buffer at pool_address (an address inside a tensor the caller keeps,
+    holding pool_tiles tiles), through tile_ids (int32 [num_tiles]) or contiguously."""
+    chk = _Checks()
+    if tile_ids is not None:
+        chk(tile_ids, "tile_ids", "i32", min_rows=num_tiles)
+    chk(sink, "sink", min_rows=num_workgroups * 8)
+    if sink.dtype not in (__import__("torch").int32, __import__("torch").uint32):
+        raise TypeError("sink: expected int32 or uint32")
+    chk.on_gpu()
+    _check(load().gqa_probe_read(ctypes.c_void_p(int(pool_address)), int(pool_tiles),
+                                 _ptr(tile_ids), int(num_tiles), int(tile_bytes),
+                                 1 if non_temporal else 0, int(num_workgroups), _ptr(sink),
+                                 _stream(sink)))
 
 
 def kv_gather(cache, block_tables, seq, num_tokens):

@@ -22,7 +22,8 @@ HIPCC_FLAGS = [
     "-mllvm", "-amdgpu-kernarg-preload-count=8",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = [os.path.join(CSRC, "gqa_paged.hip")]
+DECODE_SOURCE = os.path.join(CSRC, "gqa_paged.hip")     # decode, append, copy and gather kernels
+SOURCES = [DECODE_SOURCE, os.path.join(CSRC, "probes.hip")]
 
 
 def hipcc() -> str:

@@ -9,6 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa_paged.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,9 +23,12 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+    """Every function the headers under include/ declare."""
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -151,6 +156,27 @@ def test_fused_append_validation(lib):
         ctypes.byref(shape), nq, P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16),
         100, 0.1, P(16), None, P(16), 1 << 30, None)
     assert mq(_shape(kv_dtype=1, num_q_heads=8, block_size=16), 17) == 2   # > block size
+
+
+def test_probe_validation(lib):
+    P = ctypes.c_void_p
+    pr = lib.gqa_probe_read
+    assert pr(P(16), 8, None, 8, 3000, 1, 1, P(16), None) == 2          # tile size
+    assert pr(None, 8, None, 8, 4096, 1, 1, P(16), None) == 1
+    assert pr(P(16), 8, None, 8, 4096, 1, 0, P(16), None) == 1          # no workgroups
+    assert pr(P(16), 8, None, 9, 4096, 1, 1, P(16), None) == 1          # stream past the pool
+    assert pr(P(8), 8, None, 8, 4096, 1, 1, P(16), None) == 1           # misaligned
+    assert pr(P(16), 8, None, 0, 4096, 1, 1, P(16), None) == 0          # nothing to read
+
+
+def test_read_status_validation(lib):
+    P = ctypes.c_void_p
+    word = ctypes.c_uint32(7)
+    rd = lib.gqa_workspace_read_status
+    assert rd(None, 1 << 20, 0, ctypes.byref(word), None) == 1
+    assert rd(P(16), 1 << 20, 0, None, None) == 1
+    assert rd(P(16), 4, 0, ctypes.byref(word), None) == 3        # the word sits at bytes 4..7
+    assert word.value == 7
 
 
 def test_workspace_init_validation(lib):

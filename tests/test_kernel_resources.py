@@ -32,7 +32,7 @@ def resources():
     flags = [f for f in build.HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
     with tempfile.TemporaryDirectory() as tmp:
         cmd = [hipcc, *flags, "--offload-device-only", "-c",
-               "-Rpass-analysis=kernel-resource-usage", *build.SOURCES,
+               "-Rpass-analysis=kernel-resource-usage", build.DECODE_SOURCE,
                "-o", os.path.join(tmp, "k.o")]
         res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-4000:]
