@@ -97,6 +97,9 @@ def load():
                                                       _P, ctypes.c_int32, ctypes.c_float, _P,
                                                       _P, _P, ctypes.c_size_t, _P]
     lib.gqa_paged_decode_append_attention.restype = ctypes.c_int
+    lib.gqa_paged_decode_attention_noalloc.argtypes = [S, _P, _P, _P, _P, _P, _P, _P,
+                                                       ctypes.c_int32, ctypes.c_float, _P, _P, _P]
+    lib.gqa_paged_decode_attention_noalloc.restype = ctypes.c_int
     lib.gqa_paged_decode_workspace_init.argtypes = [S, ctypes.c_int32, _P, ctypes.c_size_t, _P]
     lib.gqa_paged_decode_workspace_init.restype = ctypes.c_int
     lib.gqa_kv_append_fp8.argtypes = [S, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P]
@@ -343,6 +346,44 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, max_
         _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
         float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, out_lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # GQA_NOALLOC_SCRATCH_BYTES
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_tables, context_lens,
+                                   max_context_len, softmax_scale=None, k_scale=None,
+                                   v_scale=None, out=None, out_lse=None, return_lse=True,
+                                   batch_invariant=False, sliding_window=0):
+    """paged_decode_attention with the library's static per-device workspace instead of
+    a caller-supplied one (the C call allocates nothing).  Calls that overlap on one
+    device race; order them on one stream."""
+    import torch
+    chk = _Checks()
+    lib = load()
+    B, Hq, D = q.shape
+    shape = make_shape(B, Hq, k_cache, block_tables, batch_invariant, sliding_window, k_scale)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if out_lse is None and return_lse:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    chk(q, "q", "bf16")
+    _, _, _, d = _pools(chk, k_cache, v_cache, k_scale, v_scale)
+    if d != D:
+        raise ValueError(f"q: head dim {D} differs from the pools' {d}")
+    chk(block_tables, "block_tables", "i32", min_rows=B)
+    chk(context_lens, "context_lens", "i32", min_rows=B)
+    chk(out, "out", "f32", (B, Hq, D))
+    if out_lse is not None:
+        chk(out_lse, "out_lse", "f32", (B, Hq))
+    chk.on_gpu()
+    _check(lib.gqa_paged_decode_attention_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), int(max_context_len),
+        float(softmax_scale), _ptr(out), _ptr(out_lse), _stream(q)))
     return out, out_lse
 
 

@@ -355,7 +355,8 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
                               const int32_t* block_tables, const int32_t* context_lens,
                               int32_t max_context_len, float softmax_scale, float* out,
                               float* out_lse, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, bool append_tail = false) {
+                              hipStream_t stream, bool append_tail = false,
+                              bool clear_counters = false) {
   gqa_status st = check_shape(s);
   if (st != GQA_OK) return st;
   if (max_context_len < 0)
@@ -447,6 +448,18 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   int32_t max_blocks_arg = s->max_blocks_per_seq;
   int32_t window_arg = s->sliding_window;
   int32_t plan_arg = target | (proportional ? 1 << 8 : 0) | num_queries << 16;
+  if (clear_counters) {
+    // A shared workspace (the static scratch): zero its arrival counters and status
+    // word with a fill kernel on the same stream, after every argument was checked.
+    uint32_t* words = p.counters;
+    size_t n = wl.cnt_words;
+    void* zargs[] = {&words, &n};
+    const unsigned zb = (unsigned)((n + 255) / 256 > 1024 ? 1024 : (n + 255) / 256);
+    const hipError_t ze = hipLaunchKernel(reinterpret_cast<const void*>(&gqa::zero_words_kernel),
+                                          dim3(zb), dim3(256), zargs, 0, stream);
+    if (ze != hipSuccess)
+      return fail(GQA_ERR_HIP, "clearing the workspace counters failed: %s", hipGetErrorString(ze));
+  }
   void* args[] = {&bt_arg, &lens_arg, &hint_arg, &max_blocks_arg, &window_arg, &plan_arg, &p};
   const hipError_t e = hipLaunchKernel(fn, dim3(launch_splits, s->num_kv_heads, s->num_seqs),
                                        dim3(waves * 64), args, 0, stream);
@@ -503,6 +516,70 @@ gqa_status gqa_paged_decode_append_attention(
   return decode_impl(s, 1, q, k_cache, v_cache, k_scale, v_scale, k_new, v_new, positions,
                      block_tables, context_lens, max_context_len, softmax_scale, out, out_lse,
                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// The workspace of gqa_paged_decode_attention_noalloc: one array per device, in
+// the library's own device memory (allocated when the code object loads, held
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// not a device address: host code uses the address hipGetSymbolAddress gives
+// for the current device, never the name.
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device.
+gqa_status scratch_address(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GQA_ERR_HIP, "noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    it = addr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_paged_decode_attention_noalloc(const gqa_paged_shape* s, const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              const float* k_scale, const float* v_scale,
+                                              const int32_t* block_tables,
+                                              const int32_t* context_lens,
+                                              int32_t max_context_len, float softmax_scale,
+                                              float* out, float* out_lse, hipStream_t stream) {
+  gqa_status st = check_shape(s);
+  if (st != GQA_OK) return st;
+  if (max_context_len < 0)
+    return fail(GQA_ERR_INVALID_ARG, "max_context_len %d < 0", max_context_len);
+  if (s->num_seqs == 0) return ok();
+  const size_t need = gqa_paged_decode_workspace_size(s, max_context_len);
+  if (need > (size_t)GQA_NOALLOC_SCRATCH_BYTES)
+    return fail(GQA_ERR_WORKSPACE, "noalloc: this call needs %zu bytes of workspace, more than "
+                "the %zu-byte static scratch (use gqa_paged_decode_attention with a workspace)",
+                need, (size_t)GQA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != GQA_OK) return st;
+  // Every call on a device shares its scratch, which keeps the last call's
+  // contents: decode_impl zeroes the counters and status word first.
+  return decode_impl(s, 1, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_scale,
+                     v_scale, nullptr, nullptr, nullptr, block_tables, context_lens,
+                     max_context_len, softmax_scale, out, out_lse, ws,
+                     (size_t)GQA_NOALLOC_SCRATCH_BYTES, stream, false, true);
 }
 
 gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* s, int32_t max_context_len,

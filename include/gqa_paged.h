@@ -345,6 +345,34 @@ gqa_status gqa_paged_decode_workspace_init(const gqa_paged_shape* shape, int32_t
                                            hipStream_t stream);
 
 /*
+ * gqa_paged_decode_attention_noalloc — gqa_paged_decode_attention without a
+ * caller-supplied workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments without workspace/workspace_bytes, same kernel
+ * and the same results bit for bit.  Its workspace is a static array of
+ * GQA_NOALLOC_SCRATCH_BYTES in the library's device memory, one per device,
+ * held until the process ends; the call allocates nothing.  A call whose
+ * workspace (gqa_paged_decode_workspace_size) exceeds that size returns
+ * GQA_ERR_WORKSPACE.  Each call first zeroes the scratch's arrival counters and
+ * status word with a small fill kernel on `stream`, then launches the decode
+ * kernel: two kernels, both capturable in a HIP graph.  All calls on one device
+ * share the array, so calls that overlap in time on one device (on different
+ * streams, or from different threads without ordering) race and give wrong
+ * results: order them on one stream.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES (32u << 20)
+gqa_status gqa_paged_decode_attention_noalloc(const gqa_paged_shape* shape,
+                                              const void* q,
+                                              const void* k_cache, const void* v_cache,
+                                              const float* k_scale, const float* v_scale,
+                                              const int32_t* block_tables,
+                                              const int32_t* context_lens,
+                                              int32_t max_context_len,
+                                              float softmax_scale,
+                                              float* out, float* out_lse,
+                                              hipStream_t stream);
+
+/*
  * gqa_workspace_read_status — the GQA_STATUS_* bits that the attention calls
  * enqueued so far on `stream` have recorded in this workspace (0: none met a bad
  * device-resident input).  Blocking: copies the word to the host after the
