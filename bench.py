@@ -19,7 +19,9 @@ least 1 GiB of other KV reads ago.
 
 Workload ``verify4`` is the verification pass of speculative decoding on the
 8K grouped-query shape: each step commits 4 new tokens (the pending one and 3
-drafts) and attends for all 4 positions, in one fused kernel.
+drafts) and attends for all 4 positions, in one fused kernel.  ``verify4_long``
+is the same on the 32K long-context shape (G = 8: 32 query rows per sequence
+and KV head).
 
 Workload ``mha_fp8_append`` is the fp8 decode step on the 40-head MHA shape:
 the quantising append of each sequence's new token (power-of-two scale per
@@ -322,7 +324,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4",
-                             "mha_fp8_append", "mha_fp8_kivi", "cow_fork"])
+                             "verify4_long", "mha_fp8_append", "mha_fp8_kivi", "cow_fork"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -363,10 +365,10 @@ def main():
 
     import numpy as np
 
-    verify = args.workload == "verify4"          # 4 query positions on the 8K shape
+    verify = args.workload in ("verify4", "verify4_long")   # 4 query positions
     fp8_append = args.workload == "mha_fp8_append"
-    base_name = {"verify4": "llama8b", "mha_fp8_append": "mha_fp8"}.get(args.workload,
-                                                                        args.workload)
+    base_name = {"verify4": "llama8b", "verify4_long": "long",
+                 "mha_fp8_append": "mha_fp8"}.get(args.workload, args.workload)
     if args.traffic_from and args.workload == "cow_fork":
         write_traffic(args.workload, args.traffic_from, fork_geometry()[5])
         return

@@ -271,14 +271,15 @@ __device__ __forceinline__ i16x4_t lds_read_transposed(const uint16_t* p) {
 // per token).
 template <int D, int BS, int M, int KV, int WAVES>
 // Launch bounds ask for two resident waves per SIMD (one 8-wave or two 4-wave
-// workgroups per CU), which caps registers at 256 per lane.
+// workgroups per CU), which caps registers at 256 per lane; variants of more
+// than 16 rows (two row tiles) need more and run one 4-wave workgroup per CU.
 //
 // block_tables [B][max_blocks]; context_lens [B]; hint_ctx: the host's bound on
 // the context lengths (it sizes the grid); window: sliding window w (0: the
 // whole context); plan_flags: the split-count target in bits 0-7, bit 8 set
 // when slots are shared out by sequence length (2 <= B <= 64), and in bits
 // 16-23 the number Q of query positions per sequence (its last Q tokens).
-__global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
+__global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_decode_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int32_t hint_ctx, int32_t max_blocks, int32_t window, int32_t plan_flags, DecodeParams p) {
   constexpr bool FP8 = KV != 0;
@@ -319,10 +320,13 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   constexpr int NN = D / 16;                 // n-tiles of the value product
   constexpr int VSTR = D + 16;
   constexpr int PRS = CT + 4;                // floats per staged weight row
-  constexpr int kMfmaWaveBytes = CT * VSTR * 2 + 16 * PRS * 4 + 16 * 4;
+  constexpr int RT = MFMA ? (M + 15) / 16 : 1;   // row tiles of 16
+  constexpr int WR = 16 * RT;                // weight rows staged per wave
+  constexpr int kMfmaWaveBytes = CT * VSTR * 2 + WR * PRS * 4 + WR * 4;
   constexpr int kWaveBytes = MFMA ? kMfmaWaveBytes : kValuWaveBytes;
   static_assert(BS % TPI == 0 && BS % 16 == 0 && kChunkTokens % CT == 0, "tile geometry");
-  static_assert(kWave % M == 0 && PPL * TSTEP * M >= NPAIR && M <= 16, "score mapping");
+  static_assert(MFMA || (kWave % M == 0 && PPL * TSTEP * M >= NPAIR && M <= 16), "score mapping");
+  static_assert(!MFMA || M <= 16 || M % 16 == 0, "matrix rows come in whole tiles of 16");
   static_assert(kWaveBytes % 16 == 0, "LDS alignment");
   using Vec = typename KVTraits<FP8>::Vec;
 
@@ -578,8 +582,9 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
   if (b != (int)blockIdx.z || s0 != hs0 || s1 != hs1)
     ids = load_ids(s0, s1, my_n, 0);               // the speculation did not apply
 
-  // Online-softmax state shared by both paths: m_ref, the reference max of this
-  // lane's head (wave-uniform per head), and l_part, this lane's share of that
+  // Online-softmax state of the vector path (the matrix path keeps one per row
+  // tile): m_ref, the reference max of this lane's head (wave-uniform per head),
+  // and l_part, this lane's share of that
   // head's exponential sum.
   float m_ref = kNegInf, l_part = 0.f;
   bool bad = false;
@@ -698,25 +703,38 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     // ---- Matrix path.  Scores C[t][g] = K q^T per 16-token tile (A = K rows,
     // B = q), value sums C[g][d] += P V (A = weights, B = V read transposed from
     // LDS).  Lane l is column hd = l & 15 and k-group qd = l >> 4 of each tile.
+    // The rows come in RT tiles of 16 (rows 16 rt .. 16 rt + 15); each K and V
+    // tile loaded serves all of them.
     const int hd = lane & 15;
     const int qd = lane >> 4;
     uint16_t* sm_v = reinterpret_cast<uint16_t*>(sm_wave);            // [CT][VSTR] bf16
-    float* sm_pw = reinterpret_cast<float*>(sm_wave + CT * VSTR * 2);  // [16][PRS] weights
-    float* sm_alpha = sm_pw + 16 * PRS;                                // [16] rescale factors
+    float* sm_pw = reinterpret_cast<float*>(sm_wave + CT * VSTR * 2);  // [WR][PRS] weights
+    float* sm_alpha = sm_pw + WR * PRS;                                // [WR] rescale factors
 
-    bf16x8_t qop[KB];                     // q of row hd, dims 8*qd + 32*kb .. +7
+    bf16x8_t qop[RT][KB];                 // q of row 16 rt + hd, dims 8*qd + 32*kb .. +7
+    int hd_limit[RT], hd_low[RT];         // row 16 rt + hd sees tokens in [low, limit)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (hd < R)
-        v = *reinterpret_cast<const uint4*>(p.q + row_index(hd) * D + 8 * qd + 32 * kb);
-      qop[kb] = as_bf16x8(v);
+    for (int rt = 0; rt < RT; ++rt) {
+      const int m = 16 * rt + hd;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (m < R)
+          v = *reinterpret_cast<const uint4*>(p.q + row_index(m) * D + 8 * qd + 32 * kb);
+        qop[rt][kb] = as_bf16x8(v);
+      }
+      hd_limit[rt] = m < R ? row_limit(m) : 0;
+      hd_low[rt] = m < R ? row_low(m) : 0;
     }
-    const int hd_limit = hd < R ? row_limit(hd) : 0;   // this lane's row sees tokens < this
-    const int hd_low = hd < R ? row_low(hd) : 0;       // and >= this
-    f32x4 acc[NN];                        // rows: heads 4*qd + r; columns: dims 16*n + hd
+    float m_t[RT], l_t[RT];               // reference max and exponential-sum share per row tile
+    f32x4 acc[RT][NN];                    // rows 16 rt + 4*qd + r; columns: dims 16*n + hd
 #pragma unroll
-    for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) {
+      m_t[rt] = kNegInf;
+      l_t[rt] = 0.f;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) acc[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // K in the A-operand layout: row (lane & 15) of a 16-token tile, dims
     // 8*qd + 32*kb .. +7 (each instruction reads 16 rows x 64 B).
@@ -752,55 +770,66 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       constexpr bool NEXT = decltype(next_tag)::value;   // chunk j+1 exists
       const int t0 = chunk_start(j);
       const int nvalid = s1 - t0;
-      const int lim = min(nvalid, hd_limit - t0);        // tokens t < lim count for row hd
-      const int lo = hd_low - t0;                        // and t >= lo
-      f32x4 sc[2];
+      f32x4 sc[RT][2];
 #pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) {
-        sc[t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          sc[t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[t16 * KB + kb]),
-                                                           qop[kb], sc[t16], 0, 0, 0);
-      }
+        for (int t16 = 0; t16 < 2; ++t16) {
+          sc[rt][t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            sc[rt][t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(kr[t16 * KB + kb]), qop[rt][kb], sc[rt][t16], 0, 0, 0);
+        }
       __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the operands just used
       if constexpr (NEXT) {
         advance_ids(j);
         issue_k(j + 1);
       }
-      // This lane's scores: head hd, tokens 16*t16 + 4*qd + r.
-      float s[8];
-      float cmax = kNegInf;
+      // This lane's scores: row 16 rt + hd, tokens 16*t16 + 4*qd + r.
+      float s[RT][8];
+      bool any_need = false;
 #pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16)
+      for (int rt = 0; rt < RT; ++rt) {
+        const int lim = min(nvalid, hd_limit[rt] - t0);  // tokens t < lim count for this row
+        const int lo = hd_low[rt] - t0;                  // and t >= lo
+        float cmax = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * t16 + 4 * qd + r;
-          float x = sc[t16][r] * p.scale_log2;
-          if (t >= lim || t < lo) x = kNegInf;  // split tail, causal limit, window, unused rows
-          s[t16 * 4 + r] = x;
-          cmax = fmaxf(cmax, x);
+        for (int t16 = 0; t16 < 2; ++t16)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * t16 + 4 * qd + r;
+            float x = sc[rt][t16][r] * p.scale_log2;
+            if (t >= lim || t < lo) x = kNegInf;  // split tail, causal limit, window, unused rows
+            s[rt][t16 * 4 + r] = x;
+            cmax = fmaxf(cmax, x);
+          }
+        cmax = max_swap32(max_swap16(cmax));   // chunk max of this row, wave-wide
+        const bool need = cmax > m_t[rt] + kLazyLog2;
+        if (__any(need)) {
+          const float m_new = need ? cmax : m_t[rt];
+          const float alpha = m_new == m_t[rt] ? 1.f : fast_exp2(m_t[rt] - m_new);
+          l_t[rt] *= alpha;
+          m_t[rt] = m_new;
+          if (lane < 16) sm_alpha[16 * rt + lane] = alpha;
+          any_need = true;
+        } else if (RT > 1 && lane < 16) {
+          sm_alpha[16 * rt + lane] = 1.f;
         }
-      cmax = max_swap32(max_swap16(cmax));   // chunk max of head hd, wave-wide
-      const bool need = cmax > m_ref + kLazyLog2;
-      const bool any_need = __any(need);
-      if (any_need) {
-        const float m_new = need ? cmax : m_ref;
-        const float alpha = m_new == m_ref ? 1.f : fast_exp2(m_ref - m_new);
-        l_part *= alpha;
-        m_ref = m_new;
-        if (lane < 16) sm_alpha[lane] = alpha;
-      }
-      float pw[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pw[k] = s[k] > kNegInf ? fast_exp2(s[k] - m_ref) : 0.f;
-        l_part += pw[k];
       }
 #pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16)
-        *reinterpret_cast<float4*>(sm_pw + hd * PRS + 16 * t16 + 4 * qd) =
-            make_float4(pw[4 * t16], pw[4 * t16 + 1], pw[4 * t16 + 2], pw[4 * t16 + 3]);
+      for (int rt = 0; rt < RT; ++rt) {
+        float pw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          pw[k] = s[rt][k] > kNegInf ? fast_exp2(s[rt][k] - m_t[rt]) : 0.f;
+          l_t[rt] += pw[k];
+        }
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16)
+          *reinterpret_cast<float4*>(sm_pw + (16 * rt + hd) * PRS + 16 * t16 + 4 * qd) =
+              make_float4(pw[4 * t16], pw[4 * t16 + 1], pw[4 * t16 + 2], pw[4 * t16 + 3]);
+      }
       // V rows to LDS (rows past the split end as zeros: their slots may hold
       // NaN poison), then the next chunk's V loads reuse the registers.
 #pragma unroll
@@ -813,25 +842,32 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
       if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs_unused, false, false);
       __builtin_amdgcn_wave_barrier();
       if (any_need) {
-        float al[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = sm_alpha[4 * qd + r];
+        for (int rt = 0; rt < RT; ++rt) {
+          float al[4];
 #pragma unroll
-        for (int n = 0; n < NN; ++n)
+          for (int r = 0; r < 4; ++r) al[r] = sm_alpha[16 * rt + 4 * qd + r];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[n][r] *= al[r];
+          for (int n = 0; n < NN; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rt][n][r] *= al[r];
+        }
       }
-      // Weights as the A operand (head hd, tokens 8*qd .. +7), split into a bf16
-      // high part and the bf16 rounding of the remainder: two products give the
-      // weights to about 16 significant bits.
-      const float4 wa = *reinterpret_cast<const float4*>(sm_pw + hd * PRS + 8 * qd);
-      const float4 wb = *reinterpret_cast<const float4*>(sm_pw + hd * PRS + 8 * qd + 4);
-      const float wf[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-      bf16x8_t whi, wlo;
+      // Weights as the A operand (row 16 rt + hd, tokens 8*qd .. +7), split into a
+      // bf16 high part and the bf16 rounding of the remainder: two products give
+      // the weights to about 16 significant bits.
+      bf16x8_t whi[RT], wlo[RT];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        whi[k] = (__bf16)wf[k];
-        wlo[k] = (__bf16)(wf[k] - (float)whi[k]);
+      for (int rt = 0; rt < RT; ++rt) {
+        const float4 wa = *reinterpret_cast<const float4*>(sm_pw + (16 * rt + hd) * PRS + 8 * qd);
+        const float4 wb =
+            *reinterpret_cast<const float4*>(sm_pw + (16 * rt + hd) * PRS + 8 * qd + 4);
+        const float wf[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          whi[rt][k] = (__bf16)wf[k];
+          wlo[rt][k] = (__bf16)(wf[k] - (float)whi[rt][k]);
+        }
       }
       // Value sums: the B operand (tokens 8*qd .. +7 of dim 16*n + hd) comes from
       // two transpose reads of the staged rows.
@@ -842,8 +878,11 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
         const i16x4_t hi = lds_read_transposed(src + 4 * VSTR);
         const bf16x8_t vop =
             __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, vop, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, vop, acc[n], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[rt], vop, acc[rt][n], 0, 0, 0);
+          acc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[rt], vop, acc[rt][n], 0, 0, 0);
+        }
       }
     };
 
@@ -862,23 +901,28 @@ __global__ __launch_bounds__(WAVES * kWave, 8 / WAVES) void paged_decode_kernel(
     }
 
     // Wave result: the products already summed over tokens; l adds over the
-    // lanes of the same head (hd).
-    const float l_wave = sum_swap32(sum_swap16(l_part));
+    // lanes of the same row.
+    float l_wave[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) l_wave[rt] = sum_swap32(sum_swap16(l_t[rt]));
     wave_bad = __any(bad);
     __syncthreads();                                 // staging area becomes sm_acc
-    // Every row below the capacity M is stored, under one branch instead of one
-    // per element: rows R..M-1 hold zeros (their weights are all zero) and are
-    // never read.  Lane group qd holds rows 4 qd .. 4 qd + 3.
-    if (4 * qd < M) {
+    // Every row below the capacity M is stored, under one branch per row tile
+    // instead of one per element: rows R..M-1 hold zeros (their weights are all
+    // zero) and are never read.  Lane group qd holds rows 16 rt + 4 qd .. + 3.
 #pragma unroll
-      for (int n = 0; n < NN; ++n)
+    for (int rt = 0; rt < RT; ++rt) {
+      if (16 * rt + 4 * qd < M) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (M >= 4 || r < M) sm_acc(wave, 4 * qd + r, 16 * n + hd) = acc[n][r];
-    }
-    if (lane < R) {
-      sm_m[wave][lane] = m_ref;
-      sm_l[wave][lane] = l_wave;
+        for (int n = 0; n < NN; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (M >= 4 || r < M) sm_acc(wave, 16 * rt + 4 * qd + r, 16 * n + hd) = acc[rt][n][r];
+      }
+      if (lane < 16 && 16 * rt + lane < R) {
+        sm_m[wave][16 * rt + lane] = m_t[rt];
+        sm_l[wave][16 * rt + lane] = l_wave[rt];
+      }
     }
   } else {
     // ---- Vector path.  LPT lanes hold one token row (8 elements each); partial

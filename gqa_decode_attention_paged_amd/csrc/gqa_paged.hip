@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <string>
@@ -123,15 +124,18 @@ int64_t max_span(const gqa_paged_shape* s, int32_t max_context_len, int32_t num_
 }
 
 // Kernel dispatch over the supported (D, BS, rows M, dtype, waves) combinations.
-// M is the row capacity, the power of two at or above G * Q: up to 16 on the
-// matrix path (bf16), up to 8 on the vector path (fp8).
-constexpr int kMaxRowsBf16 = 16;
+// M is the row capacity, the power of two at or above G * Q: up to 32 on the
+// matrix path (bf16; 32 rows are two row tiles and run on 4-wave workgroups
+// only), up to 8 on the vector path (fp8).
+constexpr int kMaxRowsBf16 = 32;
 constexpr int kMaxRowsFp8 = 8;
 
 // kv: 0 bf16, 1 fp8 with (block, KV head) scales, 2 fp8 with the KIVI layout.
 template <int D, int BS, int M, int W>
 const void* pick_kernel_m(int kv) {
-  if constexpr (M > kMaxRowsFp8) {
+  if constexpr (M > 16 && W != 4) {
+    return nullptr;
+  } else if constexpr (M > kMaxRowsFp8) {
     return kv ? nullptr : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 0, W>);
   } else {
     switch (kv) {
@@ -151,6 +155,7 @@ const void* pick_kernel_bs(int M, int fp8) {
     case 4: return pick_kernel_m<D, BS, 4, W>(fp8);
     case 8: return pick_kernel_m<D, BS, 8, W>(fp8);
     case 16: return pick_kernel_m<D, BS, 16, W>(fp8);
+    case 32: return pick_kernel_m<D, BS, 32, W>(fp8);
   }
   return nullptr;
 }
@@ -181,8 +186,34 @@ const void* pick_kernel(int D, int BS, int M, int fp8, int waves) {
 // device, so the host cannot tell the two apart.
 int target_splits(const gqa_paged_shape* s, const void* fn, int threads);
 
+// Tuning overrides, read once from the environment (unset or invalid: the
+// defaults): GQA_WAVES = 4 or 8 waves per workgroup; GQA_SPLIT_ROUNDS = r > 0
+// sizes the split target for r rounds of the resident-workgroup capacity.
+// Neither applies to batch-invariant calls.  Results change in the last bits
+// with either, as with any other split plan.
+int env_override(const char* name, int lo, int hi) {
+  const char* v = getenv(name);
+  if (!v || !*v) return 0;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  return (*end == 0 && x >= lo && x <= hi) ? (int)x : 0;
+}
+int waves_override() {
+  static const int w = [] {
+    const int x = env_override("GQA_WAVES", 4, 8);
+    return x == 4 || x == 8 ? x : 0;
+  }();
+  return w;
+}
+int rounds_override() {
+  static const int r = env_override("GQA_SPLIT_ROUNDS", 1, 64);
+  return r;
+}
+
 int pick_waves(const gqa_paged_shape* s, int row_cap, int kv) {
+  if (row_cap > 16) return 4;          // two row tiles: one 4-wave workgroup per CU
   if (s->flags & GQA_FLAG_BATCH_INVARIANT) return 4;
+  if (waves_override()) return waves_override();
   if (s->num_seqs >= 2) {
     const void* fn8 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 8);
     if (fn8 && target_splits(s, fn8, 8 * 64) <= 2) return 4;
@@ -220,7 +251,8 @@ int target_splits(const gqa_paged_shape* s, const void* fn, int threads) {
   const int cap = resident_workgroups(fn, threads);
   if (cap <= 0) return gqa::kMaxSplits;
   const int64_t pairs = (int64_t)s->num_seqs * s->num_kv_heads;
-  int64_t t = cap / pairs;            // never more workgroups than fit at once
+  const int rounds = rounds_override() ? rounds_override() : 1;
+  int64_t t = (int64_t)rounds * cap / pairs;   // one round: never more workgroups than fit
   if (t < 1) t = 1;
   if (t > gqa::kMaxSplits) t = gqa::kMaxSplits;
   return (int)t;

@@ -62,6 +62,11 @@
  *    attention calls also record each such fault as a GQA_STATUS_* bit in the
  *    workspace's status word, which gqa_workspace_read_status returns, so the
  *    host can tell a corrupted table or length from NaN data.
+ *  - Tuning overrides, read once per process from the environment: GQA_WAVES
+ *    (4 or 8 waves per workgroup) and GQA_SPLIT_ROUNDS (r >= 1: size the context
+ *    split target for r rounds of the GPU's resident workgroups instead of one).
+ *    Unset, the library chooses; neither applies under GQA_FLAG_BATCH_INVARIANT.
+ *    Like any split plan they change results in the last bits only.
  */
 #ifndef GQA_PAGED_H
 #define GQA_PAGED_H
@@ -250,7 +255,7 @@ size_t gqa_paged_multi_query_workspace_size(const gqa_paged_shape* shape, int32_
  * gqa_paged_decode_multi_query — attention for Q consecutive query positions
  * per sequence over the paged cache, as in the verification pass of
  * speculative decoding or a short chunk of prefill onto a cache.
- *   num_queries   Q >= 1, with G * Q <= 16 for bf16 pools and <= 8 for fp8
+ *   num_queries   Q >= 1, with G * Q <= 32 for bf16 pools and <= 8 for fp8
  *                 (else GQA_ERR_UNSUPPORTED)
  *   q             [B][Q][H_q][d_h] bf16; query i of sequence b sits at position
  *                 context_lens[b] - Q + i, so the Q new tokens must already be

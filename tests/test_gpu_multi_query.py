@@ -44,6 +44,9 @@ def _verify_step(gqa, case, dev, max_context_len=None, batch_invariant=False):
     (16, 8, 3, 64, 16, "bf16"),      # 6 rows in an 8-row tile
     (32, 8, 3, 128, 16, "bf16"),     # 12 rows in a 16-row tile
     (8, 8, 1, 128, 32, "bf16"),      # one row: the vector path
+    (64, 8, 4, 128, 32, "bf16"),     # G=8, 4 positions: 32 rows, two row tiles (the 32K shape)
+    (32, 8, 8, 128, 16, "bf16"),     # G=4, 8 positions: 32 rows
+    (64, 8, 3, 64, 16, "bf16"),      # 24 rows in a 32-row capacity, d=64
     (4, 4, 2, 128, 16, "fp8"),
     (16, 4, 2, 64, 32, "fp8"),
     (8, 8, 8, 128, 16, "fp8"),
@@ -130,8 +133,9 @@ def test_malformed_and_empty_contexts(gpu):
     assert_parity(out[keep], lse[keep], ref[keep], ref_lse[keep], "valid sequences")
 
 
-@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 5, "bf16"), (16, 8, 5, "fp8")])
+@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 9, "bf16"), (16, 8, 5, "fp8")])
 def test_too_many_rows_is_unsupported(gpu, hq, hkv, nq, dt):
+    """More than 32 rows (G * Q) for bf16 pools, or 8 for fp8, is refused."""
     spec = small_spec(num_seqs=1, num_q_heads=hq, num_kv_heads=hkv, head_dim=64, block_size=16,
                       kv_dtype=dt, context=64, case_id=6300)
     case = make_multi_query_case(spec, nq, seed=6, append=False)
@@ -160,6 +164,22 @@ def test_batch_invariant_mode(gpu):
     assert np.array_equal(o1[0], out[2]) and np.array_equal(l1[0], lse[2])
 
 
+def test_speculative_verify_long_context_g8(gpu):
+    """The 32K long-context shape (B=4, 64/8 heads, d=128, block 32) verifying 3
+    drafts plus the pending token: 32 rows per (sequence, KV head), fused append."""
+    spec = small_spec(num_seqs=4, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
+                      context=32772, case_id=6550)
+    case = make_multi_query_case(spec, 4, seed=8)
+    ref, ref_lse = _reference(case)
+    d = to_device(case)
+    out, lse = gpu.paged_decode_multi_query_append(d["q"], d["k_new"], d["v_new"], d["k_cache"],
+                                                   d["v_cache"], d["block_tables"],
+                                                   d["context_lens"], 32772)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                  ref, ref_lse, "verify 32K G=8")
+
+
 def test_speculative_verify_full_size(gpu):
     """The 8K grouped-query shape (B=1, 32/8 heads, d=128) verifying 3 drafts plus the
     pending token: 4 positions appended, then attended."""
@@ -172,7 +192,7 @@ def test_speculative_verify_full_size(gpu):
 
 
 @pytest.mark.parametrize("hq,hkv,nq,bs", [(32, 8, 4, 16), (64, 8, 2, 32), (8, 8, 16, 16),
-                                          (16, 8, 3, 16)])
+                                          (16, 8, 3, 16), (64, 8, 4, 32)])
 def test_fused_verify_step_matches_two_calls_bitwise(gpu, hq, hkv, nq, bs):
     """Fused append + multi-position attention equals the append followed by the
     attention call, bit for bit, and leaves the same cache."""
