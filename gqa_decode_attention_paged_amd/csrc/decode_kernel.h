@@ -257,6 +257,24 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Eight elements as a bf16 MFMA operand: bf16 bits as they are, or eight E4M3
+// codes widened exactly (an E4M3 value has at most 4 significant bits, so the
+// upper half of its fp32 form is its bf16 form; v_perm packs two upper halves).
+__device__ __forceinline__ bf16x8_t widen_to_bf16x8(uint4 v) { return as_bf16x8(v); }
+__device__ __forceinline__ bf16x8_t widen_to_bf16x8(uint2 v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t x = h ? v.y : v.x;
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x), false);   // codes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x), true);    // codes 2, 3
+    w[2 * h] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+    w[2 * h + 1] =
+        __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
 // gfx950 LDS transpose read of 16-bit elements.  Within each 16-lane group, lane
 // 16q + 4r + c receives element c of the 8-byte pieces addressed by lanes
 // 16q + 4k + r, k = 0..3.  So when those lanes address row t0 + k, column n0 + 4r
@@ -288,9 +306,9 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   constexpr bool KIVI = KV == 2;
   // M is the row capacity: the rows of one (sequence, KV head) are its query
   // positions times its G query heads, row m = i*G + g (R = G*Q <= M of them).
-  // bf16 pools with two or more rows use the matrix path; fp8 pools and single
-  // rows the vector path.
-  constexpr bool MFMA = !FP8 && M >= 2;
+  // Two or more rows use the matrix path (bf16 pools, and fp8 pools with one
+  // scale per (block, KV head)); single rows and KIVI pools the vector path.
+  constexpr bool MFMA = !KIVI && M >= 2;
   // Slots shared out by sequence length.  The matrix path branches on the
   // preloaded copy of the flag (bit 8 of plan_flags), so the uniform path does
   // not wait for the argument segment; on the vector path that copy costs 16-34
@@ -737,9 +755,14 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     }
 
     // K in the A-operand layout: row (lane & 15) of a 16-token tile, dims
-    // 8*qd + 32*kb .. +7 (each instruction reads 16 rows x 64 B).
-    const uint32_t k_lane_off = (uint32_t)((hd * D + 8 * qd) * 2);
-    uint4 kr[NK];
+    // 8*qd + 32*kb .. +7 (each instruction reads 16 rows x 64 B of bf16, or
+    // 16 rows x 32 B of fp8 codes, widened to bf16 before the product).  fp8:
+    // ks[t16] is the K scale of the block holding 16-token tile t16 (a block of
+    // 16 or 32 tokens holds whole tiles); it multiplies that tile's scores.
+    const uint32_t k_lane_off = (uint32_t)((hd * D + 8 * qd) * ESZ);
+    using KOp = typename KVTraits<FP8>::Vec;  // 8 elements: uint4 (bf16) or uint2 (fp8)
+    KOp kr[NK];
+    float ks[FP8 ? 2 : 1];
     auto issue_k_with = [&](auto policy, int j) __attribute__((always_inline)) {
       const int t0 = chunk_start(j);
 #pragma unroll
@@ -748,11 +771,23 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         const auto rsrc = tile_rsrc(j, e, kbase, true);
         const int first = (t0 + 16 * t16) % BS;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          kr[t16 * KB + kb] = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_lane_off,
+        for (int kb = 0; kb < KB; ++kb) {
+          if constexpr (FP8)
+            kr[t16 * KB + kb] = __builtin_bit_cast(
+                KOp, __builtin_amdgcn_raw_buffer_load_b64(rsrc, k_lane_off, first * D + 32 * kb,
+                                                          decltype(policy)::value));
+          else
+            kr[t16 * KB + kb] = __builtin_bit_cast(
+                KOp, __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_lane_off,
                                                            (first * D + 32 * kb) * 2,
                                                            decltype(policy)::value));
+        }
+        if constexpr (FP8) {
+          int phys = block_id(j, e);
+          phys = (unsigned)phys < (unsigned)p.num_blocks ? phys : 0;
+          ks[t16] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+              kscale_rsrc, 0, (phys * p.num_kv_heads + kvh) * 4, 0));
+        }
       }
     };
     auto issue_k = [&](int j) __attribute__((always_inline)) {
@@ -762,7 +797,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         issue_k_with(DefaultPolicy{}, j);
     };
     Vec vr[NI];
-    float vs_unused[NI];
+    float vsc[NI];                           // fp8: V scale of each row instruction's block
     const int k4 = hd >> 2, r4 = lane & 3;   // transpose-read source row / column piece
 
     auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
@@ -771,16 +806,25 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       const int t0 = chunk_start(j);
       const int nvalid = s1 - t0;
       f32x4 sc[RT][2];
+      float smul[2];                       // score multiplier of each 16-token tile
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int t16 = 0; t16 < 2; ++t16) {
+        bf16x8_t ka[KB];
 #pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16) {
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = widen_to_bf16x8(kr[t16 * KB + kb]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
           sc[rt][t16] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
-            sc[rt][t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(kr[t16 * KB + kb]), qop[rt][kb], sc[rt][t16], 0, 0, 0);
+            sc[rt][t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[rt][kb],
+                                                                 sc[rt][t16], 0, 0, 0);
         }
+        if constexpr (FP8)
+          smul[t16] = p.scale_log2 * ks[t16];
+        else
+          smul[t16] = p.scale_log2;
+      }
       __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the operands just used
       if constexpr (NEXT) {
         advance_ids(j);
@@ -799,7 +843,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = 16 * t16 + 4 * qd + r;
-            float x = sc[rt][t16][r] * p.scale_log2;
+            float x = sc[rt][t16][r] * smul[t16];
             if (t >= lim || t < lo) x = kNegInf;  // split tail, causal limit, window, unused rows
             s[rt][t16 * 4 + r] = x;
             cmax = fmaxf(cmax, x);
@@ -825,10 +869,15 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
           pw[k] = s[rt][k] > kNegInf ? fast_exp2(s[rt][k] - m_t[rt]) : 0.f;
           l_t[rt] += pw[k];
         }
+        // fp8: the value sums take the weights times the V scale of the tile's
+        // block (the exponential sum above takes them unscaled).
 #pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16)
+        for (int t16 = 0; t16 < 2; ++t16) {
+          const float vm = FP8 ? vsc[t16 * (NI / 2)] : 1.f;
           *reinterpret_cast<float4*>(sm_pw + (16 * rt + hd) * PRS + 16 * t16 + 4 * qd) =
-              make_float4(pw[4 * t16], pw[4 * t16 + 1], pw[4 * t16 + 2], pw[4 * t16 + 3]);
+              make_float4(pw[4 * t16] * vm, pw[4 * t16 + 1] * vm, pw[4 * t16 + 2] * vm,
+                          pw[4 * t16 + 3] * vm);
+        }
       }
       // V rows to LDS (rows past the split end as zeros: their slots may hold
       // NaN poison), then the next chunk's V loads reuse the registers.
@@ -836,10 +885,11 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       for (int i = 0; i < NI; ++i) {
         Vec v = vr[i];
         if (SLOW && i * TPI + row >= nvalid) v = Vec{};
-        *reinterpret_cast<Vec*>(sm_v + (i * TPI + row) * VSTR + 8 * col) = v;
+        *reinterpret_cast<uint4*>(sm_v + (i * TPI + row) * VSTR + 8 * col) =
+            __builtin_bit_cast(uint4, widen_to_bf16x8(v));
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vs_unused, false, false);
+      if constexpr (NEXT) issue_rows(j + 1, vbase, vr, vsc, false, false);
       __builtin_amdgcn_wave_barrier();
       if (any_need) {
 #pragma unroll
@@ -890,7 +940,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     // V(j+1) as soon as V(j) is staged in LDS.
     if (my_n > 0) {
       issue_k(0);
-      issue_rows(0, vbase, vr, vs_unused, false, false);
+      issue_rows(0, vbase, vr, vsc, false, false);
     }
     for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
     if (my_n > 0) {

@@ -125,18 +125,23 @@ int64_t max_span(const gqa_paged_shape* s, int32_t max_context_len, int32_t num_
 
 // Kernel dispatch over the supported (D, BS, rows M, dtype, waves) combinations.
 // M is the row capacity, the power of two at or above G * Q: up to 32 on the
-// matrix path (bf16; 32 rows are two row tiles and run on 4-wave workgroups
-// only), up to 8 on the vector path (fp8).
-constexpr int kMaxRowsBf16 = 32;
-constexpr int kMaxRowsFp8 = 8;
+// matrix path (bf16 pools and fp8 pools with per-(block, head) scales; 32 rows
+// are two row tiles and run on 4-wave workgroups only), up to 8 for KIVI pools
+// (vector path).
+constexpr int kMaxRows = 32;
+constexpr int kMaxRowsKivi = 8;
 
 // kv: 0 bf16, 1 fp8 with (block, KV head) scales, 2 fp8 with the KIVI layout.
 template <int D, int BS, int M, int W>
 const void* pick_kernel_m(int kv) {
   if constexpr (M > 16 && W != 4) {
     return nullptr;
-  } else if constexpr (M > kMaxRowsFp8) {
-    return kv ? nullptr : reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 0, W>);
+  } else if constexpr (M > kMaxRowsKivi) {
+    switch (kv) {
+      case 0: return reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 0, W>);
+      case 1: return reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 1, W>);
+    }
+    return nullptr;
   } else {
     switch (kv) {
       case 0: return reinterpret_cast<const void*>(&gqa::paged_decode_kernel<D, BS, M, 0, W>);
@@ -410,9 +415,9 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
     return fail(GQA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for bf16 pools");
   const int G = s->num_q_heads / s->num_kv_heads;
   if (num_queries < 1) return fail(GQA_ERR_INVALID_ARG, "num_queries %d < 1", num_queries);
-  if ((int64_t)G * num_queries > (fp8 ? kMaxRowsFp8 : kMaxRowsBf16))
+  if ((int64_t)G * num_queries > (kivi ? kMaxRowsKivi : kMaxRows))
     return fail(GQA_ERR_UNSUPPORTED, "G * num_queries = %lld rows exceeds %d for this KV dtype",
-                (long long)G * num_queries, fp8 ? kMaxRowsFp8 : kMaxRowsBf16);
+                (long long)G * num_queries, kivi ? kMaxRowsKivi : kMaxRows);
   const int rows = G * num_queries;
   if (append_tail && num_queries > s->block_size)
     return fail(GQA_ERR_UNSUPPORTED, "the fused append takes at most block_size (%d) tokens",

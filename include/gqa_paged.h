@@ -255,7 +255,7 @@ size_t gqa_paged_multi_query_workspace_size(const gqa_paged_shape* shape, int32_
  * gqa_paged_decode_multi_query — attention for Q consecutive query positions
  * per sequence over the paged cache, as in the verification pass of
  * speculative decoding or a short chunk of prefill onto a cache.
- *   num_queries   Q >= 1, with G * Q <= 32 for bf16 pools and <= 8 for fp8
+ *   num_queries   Q >= 1, with G * Q <= 32 (<= 8 for GQA_KV_FP8_E4M3_KIVI pools)
  *                 (else GQA_ERR_UNSUPPORTED)
  *   q             [B][Q][H_q][d_h] bf16; query i of sequence b sits at position
  *                 context_lens[b] - Q + i, so the Q new tokens must already be

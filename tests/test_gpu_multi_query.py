@@ -50,6 +50,9 @@ def _verify_step(gqa, case, dev, max_context_len=None, batch_invariant=False):
     (4, 4, 2, 128, 16, "fp8"),
     (16, 4, 2, 64, 32, "fp8"),
     (8, 8, 8, 128, 16, "fp8"),
+    (64, 8, 4, 128, 32, "fp8"),      # fp8, G=8, 4 positions: 32 rows (matrix path)
+    (32, 8, 4, 128, 16, "fp8"),      # fp8, 16 rows
+    (16, 8, 3, 64, 16, "fp8"),       # fp8, 6 rows, d=64
 ])
 def test_multi_query_parity(gpu, hq, hkv, nq, d, bs, dt):
     lens = [nq, nq + 1, 100, 1000, 3000]
@@ -133,9 +136,10 @@ def test_malformed_and_empty_contexts(gpu):
     assert_parity(out[keep], lse[keep], ref[keep], ref_lse[keep], "valid sequences")
 
 
-@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 9, "bf16"), (16, 8, 5, "fp8")])
+@pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 9, "bf16"), (32, 8, 9, "fp8"),
+                                          (16, 8, 5, "fp8_kivi")])
 def test_too_many_rows_is_unsupported(gpu, hq, hkv, nq, dt):
-    """More than 32 rows (G * Q) for bf16 pools, or 8 for fp8, is refused."""
+    """More than 32 rows (G * Q), or 8 for KIVI pools, is refused."""
     spec = small_spec(num_seqs=1, num_q_heads=hq, num_kv_heads=hkv, head_dim=64, block_size=16,
                       kv_dtype=dt, context=64, case_id=6300)
     case = make_multi_query_case(spec, nq, seed=6, append=False)
