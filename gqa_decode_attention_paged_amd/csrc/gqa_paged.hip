@@ -215,14 +215,27 @@ int rounds_override() {
   return r;
 }
 
-int pick_waves(const gqa_paged_shape* s, int row_cap, int kv) {
+int resident_workgroups(const void* fn, int threads);
+
+int pick_waves(const gqa_paged_shape* s, int row_cap, int kv, bool fused_append) {
   if (row_cap > 16) return 4;          // two row tiles: one 4-wave workgroup per CU
   if (s->flags & GQA_FLAG_BATCH_INVARIANT) return 4;
   if (waves_override()) return waves_override();
-  if (s->num_seqs >= 2) {
-    const void* fn8 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 8);
-    if (fn8 && target_splits(s, fn8, 8 * 64) <= 2) return 4;
-  }
+  const void* fn8 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 8);
+  const void* fn4 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 4);
+  if (!fn8) return 4;
+  if (s->num_seqs >= 2 && target_splits(s, fn8, 8 * 64) <= 2) return 4;
+  // More resident waves with four-wave workgroups: a variant whose registers
+  // allow an odd number of waves per SIMD (the fp8 single-row variant fits 5)
+  // leaves one idle under eight-wave workgroups.  On the 40-head fp8 MHA
+  // workload that is 56.2 against 57.6 us; where the counts tie, eight waves
+  // keep half as many partials to merge.  The same step with the fused
+  // quantising append measured the other way (59.8 against 58.0 us), so it
+  // keeps eight.
+  if (!fused_append && fn4 &&
+      (int64_t)resident_workgroups(fn4, 4 * 64) * 4 >
+          (int64_t)resident_workgroups(fn8, 8 * 64) * 8)
+    return 4;
   return 8;
 }
 
@@ -437,7 +450,8 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
                 wl.total);
   if (!aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  const int waves = pick_waves(s, row_capacity(rows), kivi ? 2 : fp8 ? 1 : 0);
+  const int waves = pick_waves(s, row_capacity(rows), kivi ? 2 : fp8 ? 1 : 0,
+                               fp8 && (positions || append_tail));
   const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows),
                                kivi ? 2 : fp8 ? 1 : 0, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
