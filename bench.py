@@ -14,8 +14,11 @@ the context with the log-sum-exp merge done by each pair's last workgroup: one
 fused kernel launch through the C ABI.  Inputs are seeded
 synthetic tensors already resident in HBM when timing starts.  To measure HBM
 rather than the 256 MB on-die Infinity Cache, consecutive steps rotate over
-enough copies of the KV pool that each step's KV bytes were last touched at
-least 1 GiB of other KV reads ago.
+copies of the KV pool, enough that a copy is read again only after 1 GiB of
+other KV reads when the timed pass has at least as many steps as copies.  A
+graph of fewer steps re-reads each of its copies once per pass, after
+(K - 1) x the step's bytes (config.reuse_distance_bytes says which; 608 MiB at
+the 8K step with K = 20, still more than twice the Infinity Cache).
 
 Workload ``verify4`` is the verification pass of speculative decoding on the
 8K grouped-query shape: each step commits 4 new tokens (the pending one and 3
@@ -529,6 +532,7 @@ def main():
             "query_positions": nq, "fp8_append": fp8_append,
             "block_table": "identity (control run)" if args.identity_table else "random permutation",
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
+            "reuse_distance_bytes": (min(copies, args.steps) - 1) * kv_bytes,
             "split_policy": "batch-invariant" if inv else "default (fills the GPU once)",
         },
         "distribution": dist,

@@ -211,7 +211,8 @@ def test_fused_fp8_append_attention(gpu, hq, hkv, d, bs):
 
 @pytest.mark.parametrize("hq,hkv,d,bs,nq", [(32, 8, 128, 16, 2), (16, 4, 64, 32, 2),
                                             (8, 8, 128, 16, 8), (40, 40, 128, 16, 4),
-                                            (8, 8, 128, 32, 8), (16, 8, 64, 32, 3)])
+                                            (8, 8, 128, 32, 8), (16, 8, 64, 32, 3),
+                                            (64, 8, 128, 32, 4), (32, 8, 128, 16, 4)])
 def test_fused_fp8_multi_query_append(gpu, hq, hkv, d, bs, nq):
     """Verification steps on an fp8 cache: Q new tokens per sequence quantised into
     the cache (possibly across a block boundary) and attended for all Q positions in

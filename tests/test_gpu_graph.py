@@ -140,3 +140,23 @@ def test_kivi_attention_and_block_copy_replay(gpu):
                                    d["context_lens"], 3000, case["softmax_scale"], d["k_scale"],
                                    d["v_scale"], out=out, workspace=ws, return_lse=False)
     _replays_match(step, [out], [d["k_cache"], d["k_scale"], d["v_scale"]])
+
+
+def test_noalloc_attention_replays(gpu):
+    """The entry point with the static workspace is two kernels (a fill of the
+    scratch's counters, then the decode kernel); both go into the graph, and every
+    replay gives the eager bits."""
+    spec = small_spec(num_seqs=3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context=("uniform", 200, 3000), case_id=7500)
+    case = make_case(spec, seed=2)
+    dev = to_device(case)
+    hint = int(case["context_lens"].max())
+    out = torch.empty((3, 32, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((3, 32), dtype=torch.float32, device=DEV)
+
+    def fn():
+        gpu.paged_decode_attention_noalloc(dev["q"], dev["k_cache"], dev["v_cache"],
+                                           dev["block_tables"], dev["context_lens"], hint,
+                                           case["softmax_scale"], out=out, out_lse=lse)
+
+    _replays_match(fn, [out, lse])

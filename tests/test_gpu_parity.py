@@ -255,3 +255,15 @@ def test_workspace_reused_across_calls(gpu):
         small[key] = case[key][:2]
     out2, lse2 = run_fused_step(gpu, to_device(small), small, max_context_len=hint, workspace=ws)
     assert_parity(out2, lse2, ref[:2], ref_lse[:2], "smaller call")
+
+
+def test_fp8_grouped_long_context_on_the_matrix_path(gpu):
+    """fp8 KV at the 32K workload's head geometry (64/8 heads, G = 8, d 128, block 32)
+    on the matrix path: codes widened to bf16, block scales folded into scores and
+    weights.  Two ragged sequences of 16385 and 9000 tokens."""
+    spec = small_spec(num_seqs=2, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
+                      kv_dtype="fp8", context=16385, case_id=7600)
+    case = make_case(spec, seed=0, context_lens=[16385, 9000])
+    ref, ref_lse = run_oracle(case)
+    out, lse = run_step(gpu, to_device(case), case)
+    assert_parity(out, lse, ref, ref_lse, "fp8 G=8 long context")

@@ -58,6 +58,8 @@ def _run(gqa, case, dev, w, max_ctx=None, fused=False):
     (40, 40, 128, 16, "fp8", 1, 700),
     (32, 8, 128, 16, "bf16", 4, 100),
     (16, 4, 64, 32, "fp8", 2, 50),
+    (64, 8, 128, 32, "bf16", 4, 1000),   # 32 rows: two row tiles
+    (64, 8, 128, 32, "fp8", 4, 300),     # fp8 on the matrix path, 32 rows
 ])
 def test_window_parity(gpu, hq, hkv, d, bs, dt, nq, w):
     lens = [8192, 3000, 100, 4097, nq]
