@@ -870,14 +870,20 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
           l_t[rt] += pw[k];
         }
         // fp8: the value sums take the weights times the V scale of the tile's
-        // block (the exponential sum above takes them unscaled).
+        // block (the exponential sum above takes them unscaled).  A masked token's
+        // weight is 0 by selection: its tile may be a stand-in block whose scale
+        // is anything, NaN included.
+        if constexpr (FP8) {
 #pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16) {
-          const float vm = FP8 ? vsc[t16 * (NI / 2)] : 1.f;
-          *reinterpret_cast<float4*>(sm_pw + (16 * rt + hd) * PRS + 16 * t16 + 4 * qd) =
-              make_float4(pw[4 * t16] * vm, pw[4 * t16 + 1] * vm, pw[4 * t16 + 2] * vm,
-                          pw[4 * t16 + 3] * vm);
+          for (int k = 0; k < 8; ++k) {
+            const float vm = vsc[(k / 4) * (NI / 2)];
+            pw[k] = s[rt][k] > kNegInf ? pw[k] * vm : 0.f;
+          }
         }
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16)
+          *reinterpret_cast<float4*>(sm_pw + (16 * rt + hd) * PRS + 16 * t16 + 4 * qd) =
+              make_float4(pw[4 * t16], pw[4 * t16 + 1], pw[4 * t16 + 2], pw[4 * t16 + 3]);
       }
       // V rows to LDS (rows past the split end as zeros: their slots may hold
       // NaN poison), then the next chunk's V loads reuse the registers.
@@ -1144,7 +1150,9 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         }
 #pragma unroll
         for (int g = 0; g < M; ++g) {
-          const float pg = FP8 ? pw[g] * vs[i] : pw[g];
+          // fp8: a masked token (weight 0) may sit in a stand-in block whose scale is
+          // anything, NaN included, so it contributes 0 by selection.
+          const float pg = FP8 ? (pw[g] != 0.f ? pw[g] * vs[i] : 0.f) : pw[g];
 #pragma unroll
           for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(pg, vf[k], acc[g][k]);
         }

@@ -267,3 +267,33 @@ def test_fp8_grouped_long_context_on_the_matrix_path(gpu):
     ref, ref_lse = run_oracle(case)
     out, lse = run_step(gpu, to_device(case), case)
     assert_parity(out, lse, ref, ref_lse, "fp8 G=8 long context")
+
+
+@pytest.mark.parametrize("hq,hkv,dt", [(4, 4, "fp8"), (16, 4, "fp8"), (16, 4, "fp8_kivi"),
+                                       (8, 8, "fp8_kivi")])
+def test_unused_block_scales_are_never_used(gpu, hq, hkv, dt):
+    """Regression: the part of a split's last chunk past its end reads a stand-in
+    block (block 0) and multiplies weights of 0 by that block's scales.  Block 0 is
+    made unused here and its scales are NaN; the outputs must still match the
+    oracle, which never reads it.  The lengths end 16 or 8 tokens into a 32-token
+    chunk; G = 1 runs the vector path, G = 4 the matrix path, and KIVI the vector
+    path with per-channel and per-token scales."""
+    lens = [48, 1000, 2064, 7]
+    spec = small_spec(num_seqs=4, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=16,
+                      kv_dtype=dt, context=2064, pool="oversized2x", case_id=7800 + hq)
+    case = make_case(spec, seed=3, context_lens=lens)
+    tab = case["block_tables"]
+    used = set(int(x) for x in tab.ravel() if x >= 0)
+    u = next(i for i in range(case["k_pool"].shape[0]) if i not in used)
+    # without an append the pool before and after it is one array: swap each once
+    arrays = {id(case[key]): case[key] for key in
+              ("k_pool", "v_pool", "k_pool_full", "v_pool_full", "k_scale", "v_scale")}
+    for a in arrays.values():
+        a[[0, u]] = a[[u, 0]]
+    tab[tab == 0] = u
+    assert 0 not in set(int(x) for x in tab.ravel())
+    case["k_scale"][0] = np.nan
+    case["v_scale"][0] = np.nan
+    ref, ref_lse = run_oracle(case)
+    out, lse = run_step(gpu, to_device(case), case)
+    assert_parity(out, lse, ref, ref_lse, f"NaN scales in unused block 0, G={hq // hkv} {dt}")
