@@ -354,6 +354,9 @@ def main():
                          "distribution (outside the headline timing)")
     ap.add_argument("--batch-invariant", action="store_true",
                     help="split every sequence by its own length only (GQA_FLAG_BATCH_INVARIANT)")
+    ap.add_argument("--split-tokens", type=int, default=0, metavar="T",
+                    help="split-length override (gqa_set_split_tokens): the batch-invariant "
+                         "plan with splits of at least T tokens")
     ap.add_argument("--no-sustained", action="store_true",
                     help="skip the read probe of the workload's tile pattern")
     ap.add_argument("--probe", action="store_true",
@@ -450,7 +453,9 @@ def main():
         k8_new, v8_new = bf16(case["fp8_k_new"][:, 0]), bf16(case["fp8_v_new"][:, 0])
         start8 = torch.from_numpy(case["fp8_start"]).to(dev)
     max_ctx = int(case["context_lens"].max())
-    inv = args.batch_invariant
+    if args.split_tokens:
+        gqa.set_split_tokens(args.split_tokens)
+    inv = args.batch_invariant or args.split_tokens > 0
     shape = gqa.make_shape(spec.num_seqs, spec.num_q_heads, k0, bt, batch_invariant=inv)
     ws = torch.zeros(max(16, gqa.multi_query_workspace_size(shape, nq, max_ctx)),
                      dtype=torch.uint8, device=dev)
@@ -533,7 +538,9 @@ def main():
             "block_table": "identity (control run)" if args.identity_table else "random permutation",
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
             "reuse_distance_bytes": (min(copies, args.steps) - 1) * kv_bytes,
-            "split_policy": "batch-invariant" if inv else "default (fills the GPU once)",
+            "split_policy": (f"batch-invariant, splits of at least {args.split_tokens} tokens"
+                             if args.split_tokens else
+                             "batch-invariant" if inv else "default (fills the GPU once)"),
         },
         "distribution": dist,
         "roofline": {

@@ -25,7 +25,7 @@ __all__ = [
     "workspace_size", "num_splits", "kv_gather", "last_error", "version", "LIB_PATH",
     "paged_decode_append_attention", "make_workspace", "workspace_init", "make_shape",
     "workspace_status", "STATUS_BAD_CONTEXT_LEN", "STATUS_CONTEXT_OVER_HINT",
-    "STATUS_BAD_BLOCK_ID", "STATUS_BAD_APPEND",
+    "STATUS_BAD_BLOCK_ID", "STATUS_BAD_APPEND", "set_split_tokens", "split_tokens",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_paged.so")
@@ -88,6 +88,10 @@ def load():
     lib.gqa_paged_decode_multi_query_append.restype = ctypes.c_int
     lib.gqa_decode_num_splits.argtypes = [ctypes.c_int32]
     lib.gqa_decode_num_splits.restype = ctypes.c_int32
+    lib.gqa_set_split_tokens.argtypes = [ctypes.c_int32]
+    lib.gqa_set_split_tokens.restype = ctypes.c_int
+    lib.gqa_split_tokens.argtypes = []
+    lib.gqa_split_tokens.restype = ctypes.c_int32
     lib.gqa_paged_decode_workspace_size.argtypes = [S, ctypes.c_int32]
     lib.gqa_paged_decode_workspace_size.restype = ctypes.c_size_t
     lib.gqa_paged_decode_attention.argtypes = [S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
@@ -243,8 +247,21 @@ def make_shape(num_seqs, num_q_heads, k_cache, block_tables, batch_invariant=Fal
 
 
 def num_splits(context_len: int) -> int:
-    """Partial attentions a sequence of this length is split into (host policy)."""
+    """Partial attentions a sequence of this length is split into under the
+    batch-invariant plan (with the split-length override, if one is set)."""
     return int(load().gqa_decode_num_splits(int(context_len)))
+
+
+def set_split_tokens(tokens: int) -> None:
+    """Set (a multiple of 32 in [128, 2^20]) or clear (0) the process-wide
+    split-length override; while set, attention calls split each sequence by its
+    own length with splits of at least that many tokens."""
+    _check(load().gqa_set_split_tokens(int(tokens)))
+
+
+def split_tokens() -> int:
+    """The current split-length override (0: none)."""
+    return int(load().gqa_split_tokens())
 
 
 def workspace_size(shape: PagedShape, max_context_len: int) -> int:

@@ -11,12 +11,12 @@ constexpr int kWave = 64;
 // Split policy.  A sequence of ctx tokens is cut into at most `target`
 // contiguous token ranges ("splits") of split_tokens tokens each (a multiple of
 // kChunkTokens, so every split starts on a block boundary for block sizes 16
-// and 32), and no split is shorter than kMinSplitTokens unless the whole
-// context is.  Each split becomes one workgroup per KV head; the splits of a
-// (sequence, KV head) are merged by log-sum-exp.  The host picks `target`:
-// either from the GPU's resident-workgroup capacity and the batch's number of
-// (sequence, KV head) pairs, or kMaxSplits when results must not depend on the
-// rest of the batch.
+// and 32), and no split is shorter than `min_tokens` (kMinSplitTokens unless
+// a split-length override is set) unless the whole context is.  Each split
+// becomes one workgroup per KV head; the splits of a (sequence, KV head) are
+// merged by log-sum-exp.  The host picks `target`: either from the GPU's
+// resident-workgroup capacity and the batch's number of (sequence, KV head)
+// pairs, or kMaxSplits when results must not depend on the rest of the batch.
 constexpr int kMaxSplits = 64;        // also the final merge's lanes per head
 constexpr int kMinSplitTokens = 128;
 constexpr int kChunkTokens = 32;      // tokens one wave handles per iteration
@@ -26,14 +26,15 @@ struct SplitPlan {
   int split_tokens;
 };
 
-__host__ __device__ inline SplitPlan split_plan(int ctx, int target = kMaxSplits) {
+__host__ __device__ inline SplitPlan split_plan(int ctx, int target = kMaxSplits,
+                                                int min_tokens = kMinSplitTokens) {
   if (ctx <= 0) return {0, 0};
-  int n = (ctx + kMinSplitTokens - 1) / kMinSplitTokens;
+  int n = (ctx - 1) / min_tokens + 1;              // ceil(ctx / min_tokens), no overflow
   if (n > target) n = target;
   if (n < 1) n = 1;
-  int st = (ctx + n - 1) / n;
+  int st = (ctx - 1) / n + 1;
   st = (st + kChunkTokens - 1) / kChunkTokens * kChunkTokens;
-  return {(ctx + st - 1) / st, st};
+  return {(ctx - 1) / st + 1, st};
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <cstdlib>
 #include <map>
 #include <mutex>
@@ -106,8 +107,8 @@ WorkspaceLayout workspace_layout(const gqa_paged_shape* s, int max_splits, int n
 // `len` under target `target`: a split plan never uses more than
 // min(target, ceil(len / kMinSplitTokens)), while the plan of `len` itself may
 // round to fewer than a shorter length's plan.
-int split_bound(int64_t len, int target) {
-  const int64_t n = (len + gqa::kMinSplitTokens - 1) / gqa::kMinSplitTokens;
+int split_bound(int64_t len, int target, int min_tokens = gqa::kMinSplitTokens) {
+  const int64_t n = (len + min_tokens - 1) / min_tokens;
   const int64_t b = n < target ? n : target;
   return b < 1 ? 1 : (int)b;
 }
@@ -189,7 +190,7 @@ const void* pick_kernel(int D, int BS, int M, int fp8, int waves) {
 // 51.9 us; the same shape with equal lengths, where the sharing has nothing to
 // balance, gives back 1% (48.2 against 47.7 us).  The lengths live on the
 // device, so the host cannot tell the two apart.
-int target_splits(const gqa_paged_shape* s, const void* fn, int threads);
+int target_splits(const gqa_paged_shape* s, const void* fn, int threads, bool invariant);
 
 // Tuning overrides, read once from the environment (unset or invalid: the
 // defaults): GQA_WAVES = 4 or 8 waves per workgroup; GQA_SPLIT_ROUNDS = r > 0
@@ -215,16 +216,32 @@ int rounds_override() {
   return r;
 }
 
+// Split-length override (GQA_SPLIT_TOKENS, or gqa_set_split_tokens at run time):
+// 0, or the shortest split in tokens, a multiple of kChunkTokens in
+// [kMinSplitTokens, kMaxSplitTokensOverride].  When set, every attention call
+// takes the batch-invariant plan with that minimum in place of kMinSplitTokens.
+constexpr int kMaxSplitTokensOverride = 1 << 20;
+bool valid_split_tokens(int t) {
+  return t >= gqa::kMinSplitTokens && t <= kMaxSplitTokensOverride && t % gqa::kChunkTokens == 0;
+}
+std::atomic<int>& split_tokens_setting() {
+  static std::atomic<int> v{[] {
+    const int x = env_override("GQA_SPLIT_TOKENS", gqa::kMinSplitTokens, kMaxSplitTokensOverride);
+    return valid_split_tokens(x) ? x : 0;
+  }()};
+  return v;
+}
+
 int resident_workgroups(const void* fn, int threads);
 
-int pick_waves(const gqa_paged_shape* s, int row_cap, int kv, bool fused_append) {
+int pick_waves(const gqa_paged_shape* s, int row_cap, int kv, bool fused_append, bool invariant) {
   if (row_cap > 16) return 4;          // two row tiles: one 4-wave workgroup per CU
-  if (s->flags & GQA_FLAG_BATCH_INVARIANT) return 4;
+  if (invariant) return 4;
   if (waves_override()) return waves_override();
   const void* fn8 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 8);
   const void* fn4 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 4);
   if (!fn8) return 4;
-  if (s->num_seqs >= 2 && target_splits(s, fn8, 8 * 64) <= 2) return 4;
+  if (s->num_seqs >= 2 && target_splits(s, fn8, 8 * 64, false) <= 2) return 4;
   // More resident waves with four-wave workgroups: a variant whose registers
   // allow an odd number of waves per SIMD (the fp8 single-row variant fits 5)
   // leaves one idle under eight-wave workgroups.  On the 40-head fp8 MHA
@@ -262,10 +279,10 @@ int resident_workgroups(const void* fn, int threads) {
 // KV head) pairs fill the resident-workgroup capacity once without exceeding
 // it (fewer, longer splits amortise each workgroup's start-up and merge, and a
 // partial second round of workgroups would only add a tail).  With
-// GQA_FLAG_BATCH_INVARIANT, the fixed maximum, so the split of a sequence
-// depends on its own length only.
-int target_splits(const gqa_paged_shape* s, const void* fn, int threads) {
-  if (s->flags & GQA_FLAG_BATCH_INVARIANT) return gqa::kMaxSplits;
+// GQA_FLAG_BATCH_INVARIANT or a split-length override, the fixed maximum, so
+// the split of a sequence depends on its own length only.
+int target_splits(const gqa_paged_shape* s, const void* fn, int threads, bool invariant) {
+  if (invariant) return gqa::kMaxSplits;
   const int cap = resident_workgroups(fn, threads);
   if (cap <= 0) return gqa::kMaxSplits;
   const int64_t pairs = (int64_t)s->num_seqs * s->num_kv_heads;
@@ -293,8 +310,20 @@ const char* gqa_last_error(void) { return g_last_error.c_str(); }
 const char* gqa_version(void) { return "gqa_paged 0.3 (gfx950)"; }
 
 int32_t gqa_decode_num_splits(int32_t context_len) {
-  return gqa::split_plan(context_len).num_splits;
+  const int t = split_tokens_setting().load(std::memory_order_relaxed);
+  return gqa::split_plan(context_len, gqa::kMaxSplits, t > 0 ? t : gqa::kMinSplitTokens).num_splits;
 }
+
+gqa_status gqa_set_split_tokens(int32_t tokens) {
+  if (tokens != 0 && !valid_split_tokens(tokens))
+    return fail(GQA_ERR_INVALID_ARG,
+                "split length %d: 0, or a multiple of %d in [%d, %d]", tokens, gqa::kChunkTokens,
+                gqa::kMinSplitTokens, kMaxSplitTokensOverride);
+  split_tokens_setting().store(tokens, std::memory_order_relaxed);
+  return ok();
+}
+
+int32_t gqa_split_tokens(void) { return split_tokens_setting().load(std::memory_order_relaxed); }
 
 size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max_context_len) {
   if (check_shape(shape) != GQA_OK || max_context_len < 0) return 0;
@@ -450,19 +479,25 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
                 wl.total);
   if (!aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  // One reading of the split-length override per call; with it, the plan is the
+  // batch-invariant one with that minimum split length.
+  const int split_tokens = split_tokens_setting().load(std::memory_order_relaxed);
+  const bool invariant = (s->flags & GQA_FLAG_BATCH_INVARIANT) || split_tokens > 0;
+  const int min_tokens = split_tokens > 0 ? split_tokens : gqa::kMinSplitTokens;
   const int waves = pick_waves(s, row_capacity(rows), kivi ? 2 : fp8 ? 1 : 0,
-                               fp8 && (positions || append_tail));
+                               fp8 && (positions || append_tail), invariant);
   const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows),
                                kivi ? 2 : fp8 ? 1 : 0, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
-  const int target = target_splits(s, fn, waves * 64);
-  const int launch_splits = split_bound(max_span(s, max_context_len, num_queries), target);
+  const int target = target_splits(s, fn, waves * 64, invariant);
+  const int launch_splits =
+      split_bound(max_span(s, max_context_len, num_queries), target, min_tokens);
   if ((int64_t)launch_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
     return fail(GQA_ERR_UNSUPPORTED, "grid too large");
   // Ragged batches: share each KV head's slots out by sequence length (one
   // lane per sequence, so up to 64 sequences) instead of giving every sequence
   // the same number of splits.
-  const bool proportional = !(s->flags & GQA_FLAG_BATCH_INVARIANT) && launch_splits >= 2 &&
+  const bool proportional = !invariant && launch_splits >= 2 &&
                             s->num_seqs >= 2 && s->num_seqs <= 64;
 
   char* ws = static_cast<char*>(workspace);
@@ -491,6 +526,7 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.num_blocks = s->num_blocks;
   p.max_splits = ws_splits;
   p.proportional = proportional ? 1 : 0;
+  p.min_split_tokens = min_tokens;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   // The leading scalar arguments of paged_decode_kernel (preloaded into SGPRs).
   const int32_t* bt_arg = block_tables;

@@ -67,6 +67,12 @@
  *    split target for r rounds of the GPU's resident workgroups instead of one).
  *    Unset, the library chooses; neither applies under GQA_FLAG_BATCH_INVARIANT.
  *    Like any split plan they change results in the last bits only.
+ *  - Split-length override: GQA_SPLIT_TOKENS (read once per process, or set at
+ *    run time with gqa_set_split_tokens) = T, a multiple of 32 in [128, 2^20].
+ *    When set, every attention call splits each sequence by its own length
+ *    with splits of at least T tokens (at most 64 of them), as under
+ *    GQA_FLAG_BATCH_INVARIANT with T in place of 128: results stay
+ *    batch-invariant, and T trades that mode's split count for its cost.
  */
 #ifndef GQA_PAGED_H
 #define GQA_PAGED_H
@@ -184,10 +190,28 @@ gqa_status gqa_kv_append_tokens(const gqa_paged_shape* shape, int32_t num_tokens
 /*
  * gqa_decode_num_splits — the batch-invariant context split plan (host
  * function, no GPU): how many partial attentions a sequence of `context_len`
- * attended tokens is cut into under GQA_FLAG_BATCH_INVARIANT.  0 for
+ * attended tokens is cut into under GQA_FLAG_BATCH_INVARIANT, with the current
+ * split-length override T if one is set (else T = 128):
+ * n = min(64, ceil(context_len / T)) splits of ceil(context_len / n) tokens
+ * rounded up to a multiple of 32, the last one shorter.  0 for
  * context_len <= 0.  No plan uses more than min(64, ceil(context_len / 128)).
+ * The split-K decomposition with a log-sum-exp merge of the pieces is that of
+ * *The Mathematics of Transformer Inference* §8 (sequence shards merged by
+ * their log-sum-exp), applied to context ranges on one GPU.
  */
 int32_t gqa_decode_num_splits(int32_t context_len);
+
+/*
+ * gqa_set_split_tokens — set (tokens = T, a multiple of 32 in [128, 2^20]) or
+ * clear (tokens = 0) the process-wide split-length override that
+ * GQA_SPLIT_TOKENS sets at start-up.  Calls made after it returns use the new
+ * value; a call already being launched on another thread may use either.
+ * Returns GQA_ERR_INVALID_ARG (and keeps the old value) for any other value.
+ * Launches captured in a HIP graph keep the plan they were captured with.
+ * gqa_split_tokens returns the current value (0 when none is set).
+ */
+gqa_status gqa_set_split_tokens(int32_t tokens);
+int32_t gqa_split_tokens(void);
 
 /*
  * gqa_paged_decode_workspace_size — bytes of device workspace that

@@ -258,12 +258,12 @@ def test_kivi_dtype_is_accepted(lib):
     assert lib.gqa_paged_decode_workspace_size(ctypes.byref(_shape(kv_dtype=3)), 1000) == 0
 
 
-def _split_plan(ctx, target=64):
+def _split_plan(ctx, target=64, min_tokens=128):
     """The split plan as the kernels apply it: at most `target` splits of a whole
-    number of 32-token chunks, none under 128 tokens unless the context is."""
+    number of 32-token chunks, none under `min_tokens` tokens unless the context is."""
     if ctx <= 0:
         return 0, 0
-    n = min(max((ctx + 127) // 128, 1), target)
+    n = min(max(-(-ctx // min_tokens), 1), target)
     st = -(-ctx // n)
     st = -(-st // 32) * 32
     return -(-ctx // st), st
@@ -291,3 +291,40 @@ def test_regression_lengths_give_a_row_no_token_of_the_last_split(lib, nq):
             last_start = (n - 1) * st
             assert last_start > ctx - nq, (ctx, nq, target)   # query 0 sits at ctx - nq
             assert last_start < ctx
+
+
+def test_split_tokens_override(lib):
+    """The split-length override: set, read back, cleared; bad values refused with
+    the old value kept; the host split plan follows it."""
+    import gqa_decode_attention_paged_amd as gqa
+    assert gqa.split_tokens() == 0
+    try:
+        for t in (128, 160, 2080, 1 << 20):
+            gqa.set_split_tokens(t)
+            assert gqa.split_tokens() == t
+            for ctx in list(range(0, 700, 7)) + [2047, 2048, 2049, 8192, 32769, 1 << 22]:
+                assert gqa.num_splits(ctx) == _split_plan(ctx, 64, t)[0], (t, ctx)
+        gqa.set_split_tokens(2080)
+        for bad in (-32, 1, 96, 127, 130, 2081, (1 << 20) + 32, 1 << 21):
+            with pytest.raises(gqa.GqaError):
+                gqa.set_split_tokens(bad)
+            assert gqa.split_tokens() == 2080
+        assert gqa.num_splits(32769) == 16                 # 16 splits of 2080 tokens
+    finally:
+        gqa.set_split_tokens(0)
+    assert gqa.split_tokens() == 0 and gqa.num_splits(32769) == _split_plan(32769)[0]
+
+
+@pytest.mark.parametrize("value,expect", [("512", 512), ("2080", 2080), ("100", 0),
+                                          ("130", 0), ("4096x", 0), ("", 0)])
+def test_split_tokens_environment(lib, value, expect):
+    """GQA_SPLIT_TOKENS is read once at start-up; invalid values leave no override."""
+    import subprocess
+    import sys
+    code = ("import gqa_decode_attention_paged_amd as g; "
+            "print(g.split_tokens(), g.num_splits(32769))")
+    env = dict(os.environ, GQA_SPLIT_TOKENS=value)
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, check=True,
+                         capture_output=True, text=True).stdout.split()
+    assert int(out[0]) == expect
+    assert int(out[1]) == _split_plan(32769, 64, expect or 128)[0]

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests._dev import to_device, run_step
+from tests._dev import assert_parity, run_fused_step, run_oracle, to_device, run_step
 from workloads import make_case, small_spec
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +68,58 @@ def test_default_mode_order_invariant_and_batch_consistent(gpu):
         one = _one(case, b)
         o1, l1 = run_step(gpu, to_device(one), one)
         assert np.max(np.abs(o1[0] - out[b])) <= 1e-5 and np.max(np.abs(l1[0] - lse[b])) <= 1e-5
+
+
+@pytest.fixture
+def split_override(gpu):
+    """The binding, with the split-length override cleared again afterwards."""
+    yield gpu
+    gpu.set_split_tokens(0)
+
+
+@pytest.mark.parametrize("tokens", [256, 1024])
+def test_split_length_override_is_batch_invariant(split_override, tokens):
+    """With a split-length override the results match the oracle, and a sequence
+    gives the same bits alone (small hint) and in the batch (large hint)."""
+    gpu = split_override
+    case = _batch_case()
+    hint = case["block_tables"].shape[1] * 16
+    ref, ref_lse = run_oracle(case)
+    gpu.set_split_tokens(tokens)
+    out, lse = run_step(gpu, to_device(case), case, max_context_len=hint)
+    assert_parity(out, lse, ref, ref_lse, f"split length {tokens}")
+    for b in (0, 3, 5):
+        one = _one(case, b)
+        o1, l1 = run_step(gpu, to_device(one), one)
+        assert np.array_equal(o1[0], out[b]) and np.array_equal(l1[0], lse[b]), b
+
+
+def test_split_length_128_is_the_batch_invariant_plan(split_override):
+    """An override of 128 tokens is the batch-invariant flag's own plan: same bits."""
+    gpu = split_override
+    case = _batch_case()
+    o_flag, l_flag = run_step(gpu, to_device(case), case, batch_invariant=True)
+    gpu.set_split_tokens(128)
+    o_t, l_t = run_step(gpu, to_device(case), case)
+    assert np.array_equal(o_flag, o_t) and np.array_equal(l_flag, l_t)
+
+
+def test_split_length_override_fused_append(split_override):
+    """The fused append step under an override (G = 8, block 32, a split boundary
+    inside the sequences): cache bits and attention against the oracle."""
+    gpu = split_override
+    spec = small_spec(num_seqs=3, num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=32,
+                      context=("uniform", 700, 3000), append=True, case_id=4002)
+    case = make_case(spec, seed=4)
+    ref, ref_lse = run_oracle(case)
+    gpu.set_split_tokens(512)
+    dev = to_device(case)
+    out, lse = run_fused_step(gpu, dev, case)
+    assert_parity(out, lse, ref, ref_lse, "fused append, split length 512")
+    import torch
+    k = dev["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    v = dev["v_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(k, case["k_pool_full"]) and np.array_equal(v, case["v_pool_full"])
 
 
 def test_fp8_codes_decode_exactly(gpu):
