@@ -234,14 +234,22 @@ std::atomic<int>& split_tokens_setting() {
 
 int resident_workgroups(const void* fn, int threads);
 
-int pick_waves(const gqa_paged_shape* s, int row_cap, int kv, bool fused_append, bool invariant) {
-  if (row_cap > 16) return 4;          // two row tiles: one 4-wave workgroup per CU
-  if (invariant) return 4;
-  if (waves_override()) return waves_override();
+// Waves per workgroup, and the waves of the variant whose resident capacity
+// sizes the split target (the same, except for one four-wave workgroup per CU).
+struct WavePlan {
+  int waves;
+  int target_waves;
+};
+
+WavePlan pick_waves(const gqa_paged_shape* s, int row_cap, int kv, bool fused_append,
+                    bool invariant) {
+  if (row_cap > 16) return {4, 4};     // two row tiles: one 4-wave workgroup per CU
+  if (invariant) return {4, 4};
+  if (waves_override()) return {waves_override(), waves_override()};
   const void* fn8 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 8);
   const void* fn4 = pick_kernel(s->head_dim, s->block_size, row_cap, kv, 4);
-  if (!fn8) return 4;
-  if (s->num_seqs >= 2 && target_splits(s, fn8, 8 * 64, false) <= 2) return 4;
+  if (!fn8) return {4, 4};
+  if (s->num_seqs >= 2 && target_splits(s, fn8, 8 * 64, false) <= 2) return {4, 4};
   // More resident waves with four-wave workgroups: a variant whose registers
   // allow an odd number of waves per SIMD (the fp8 single-row variant fits 5)
   // leaves one idle under eight-wave workgroups.  On the 40-head fp8 MHA
@@ -252,8 +260,18 @@ int pick_waves(const gqa_paged_shape* s, int row_cap, int kv, bool fused_append,
   if (!fused_append && fn4 &&
       (int64_t)resident_workgroups(fn4, 4 * 64) * 4 >
           (int64_t)resident_workgroups(fn8, 8 * 64) * 8)
-    return 4;
-  return 8;
+    return {4, 4};
+  // One four-wave workgroup per CU, at the eight-wave split count, where the
+  // matrix path's work per byte is light: bf16 up to 8 rows, fp8 (whose codes
+  // are widened first) up to 4.  Four waves stream as fast as eight there, and
+  // the workgroup has half as many waves to start and to merge: 8K, G = 4:
+  // 13.2 against 13.9 us; 32K, G = 8: 85.3 against 86.1; fp8 8K, G = 4: 12.3
+  // against 12.5.  Heavier rows need the second wave per SIMD to hide their
+  // compute: fp8 32K, G = 8: 70.9 against 62.9 us; 16 rows (8K, 4 positions,
+  // G = 4): 20.5 against 18.1.
+  const bool matrix = kv != 2 && row_cap >= 2;
+  if (matrix && fn4 && row_cap * (kv == 1 ? 2 : 1) <= 8) return {4, 8};
+  return {8, 8};
 }
 
 // Workgroups of `fn` the current device keeps resident at once (compute units
@@ -484,12 +502,18 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   const int split_tokens = split_tokens_setting().load(std::memory_order_relaxed);
   const bool invariant = (s->flags & GQA_FLAG_BATCH_INVARIANT) || split_tokens > 0;
   const int min_tokens = split_tokens > 0 ? split_tokens : gqa::kMinSplitTokens;
-  const int waves = pick_waves(s, row_capacity(rows), kivi ? 2 : fp8 ? 1 : 0,
-                               fp8 && (positions || append_tail), invariant);
-  const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows),
-                               kivi ? 2 : fp8 ? 1 : 0, waves);
+  const int kv = kivi ? 2 : fp8 ? 1 : 0;
+  const WavePlan wp = pick_waves(s, row_capacity(rows), kv, fp8 && (positions || append_tail),
+                                 invariant);
+  const int waves = wp.waves;
+  const void* fn = pick_kernel(s->head_dim, s->block_size, row_capacity(rows), kv, waves);
   if (!fn) return fail(GQA_ERR_UNSUPPORTED, "no kernel for this shape");
-  const int target = target_splits(s, fn, waves * 64, invariant);
+  const void* tfn = wp.target_waves == waves
+                        ? fn
+                        : pick_kernel(s->head_dim, s->block_size, row_capacity(rows), kv,
+                                      wp.target_waves);
+  const int target = target_splits(s, tfn ? tfn : fn, (tfn ? wp.target_waves : waves) * 64,
+                                   invariant);
   const int launch_splits =
       split_bound(max_span(s, max_context_len, num_queries), target, min_tokens);
   if ((int64_t)launch_splits * s->num_kv_heads * s->num_seqs > INT32_MAX)
