@@ -346,6 +346,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   static_assert(BS % TPI == 0 && BS % 16 == 0 && kChunkTokens % CT == 0, "tile geometry");
   static_assert(MFMA || (kWave % M == 0 && PPL * TSTEP * M >= NPAIR && M <= 16), "score mapping");
   static_assert(!MFMA || M <= 16 || M % 16 == 0, "matrix rows come in whole tiles of 16");
+  static_assert(!MFMA || !FP8 || KB % 2 == 0, "fp8 K pieces hold two score steps");
   static_assert(kWaveBytes % 16 == 0, "LDS alignment");
   using Vec = typename KVTraits<FP8>::Vec;
 
@@ -730,7 +731,15 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     float* sm_pw = reinterpret_cast<float*>(sm_wave + CT * VSTR * 2);  // [WR][PRS] weights
     float* sm_alpha = sm_pw + WR * PRS;                                // [WR] rescale factors
 
-    bf16x8_t qop[RT][KB];                 // q of row 16 rt + hd, dims 8*qd + 32*kb .. +7
+    // The product sums over all D dims, so any assignment of dims to (kb, qd,
+    // element) serves, as long as K and q share it.  bf16: step kb, lane group
+    // qd holds dims 32*kb + 8*qd .. +7 (each K row piece is 16 bytes, four lanes
+    // read 64 contiguous bytes of a row).  fp8: dims 64*(kb/2) + 16*qd +
+    // 8*(kb%2) .. +7, so one 16-byte load per lane fetches two steps' codes and
+    // four lanes again read 64 contiguous bytes of a row (with the bf16 mapping
+    // an fp8 row piece would be 8 bytes: twice the cache-line requests per byte).
+    auto kdim = [&](int kb) { return FP8 ? 64 * (kb >> 1) + 16 * qd + 8 * (kb & 1) : 32 * kb + 8 * qd; };
+    bf16x8_t qop[RT][KB];                 // q of row 16 rt + hd, dims kdim(kb) .. +7
     int hd_limit[RT], hd_low[RT];         // row 16 rt + hd sees tokens in [low, limit)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -739,7 +748,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       for (int kb = 0; kb < KB; ++kb) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (m < R)
-          v = *reinterpret_cast<const uint4*>(p.q + row_index(m) * D + 8 * qd + 32 * kb);
+          v = *reinterpret_cast<const uint4*>(p.q + row_index(m) * D + kdim(kb));
         qop[rt][kb] = as_bf16x8(v);
       }
       hd_limit[rt] = m < R ? row_limit(m) : 0;
@@ -756,11 +765,11 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     }
 
     // K in the A-operand layout: row (lane & 15) of a 16-token tile, dims
-    // 8*qd + 32*kb .. +7 (each instruction reads 16 rows x 64 B of bf16, or
-    // 16 rows x 32 B of fp8 codes, widened to bf16 before the product).  fp8:
-    // ks[t16] is the K scale of the block holding 16-token tile t16 (a block of
-    // 16 or 32 tokens holds whole tiles); it multiplies that tile's scores.
-    const uint32_t k_lane_off = (uint32_t)((hd * D + 8 * qd) * ESZ);
+    // kdim(kb) .. +7 (each instruction reads 16 rows x 64 B: bf16 for one step,
+    // fp8 codes for two, widened to bf16 before the product).  fp8: ks[t16] is
+    // the K scale of the block holding 16-token tile t16 (a block of 16 or 32
+    // tokens holds whole tiles); it multiplies that tile's scores.
+    const uint32_t k_lane_off = (uint32_t)((hd * D + (FP8 ? 16 : 8) * qd) * ESZ);
     using KOp = typename KVTraits<FP8>::Vec;  // 8 elements: uint4 (bf16) or uint2 (fp8)
     KOp kr[NK];
     float ks[FP8 ? 2 : 1];
@@ -771,13 +780,18 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         const int e = CT >= BS ? (16 * t16) / BS : 0;
         const auto rsrc = tile_rsrc(j, e, kbase, true);
         const int first = (t0 + 16 * t16) % BS;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          if constexpr (FP8)
-            kr[t16 * KB + kb] = __builtin_bit_cast(
-                KOp, __builtin_amdgcn_raw_buffer_load_b64(rsrc, k_lane_off, first * D + 32 * kb,
-                                                          decltype(policy)::value));
-          else
+          for (int h = 0; h < KB / 2; ++h) {       // steps 2h and 2h + 1
+            const uint4 w = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_lane_off, first * D + 64 * h,
+                                                             decltype(policy)::value));
+            kr[t16 * KB + 2 * h] = make_uint2(w.x, w.y);
+            kr[t16 * KB + 2 * h + 1] = make_uint2(w.z, w.w);
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
             kr[t16 * KB + kb] = __builtin_bit_cast(
                 KOp, __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_lane_off,
                                                            (first * D + 32 * kb) * 2,
