@@ -34,6 +34,10 @@ Workload ``mha_fp8_kivi`` is the 40-head MHA shape with the KIVI scale layout
 (keys scaled per channel of each block, values per token); its bytes include
 those scales.
 
+Workload ``long_fp8`` is the 32K grouped-query shape (B = 4, 64/8 heads, block
+32, 32768 tokens) over an fp8 pool with one scale per (block, KV head), no
+append: the matrix path's fp8 variant at G = 8.
+
 Workload ``cow_fork`` measures the copy-on-write block copy instead: 256 prompts
 on the 8K grouped-query pool geometry each fork into 8 parallel samples, so each
 prompt's partially filled last block is copied to 7 fresh blocks (1792 copies,
@@ -327,7 +331,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=["tiny", "llama8b", "batched", "long", "mha_fp8", "verify4",
-                             "verify4_long", "mha_fp8_append", "mha_fp8_kivi", "cow_fork"])
+                             "verify4_long", "mha_fp8_append", "mha_fp8_kivi", "long_fp8",
+                             "cow_fork"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

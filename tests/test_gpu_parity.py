@@ -18,7 +18,7 @@ from workloads import make_case, small_spec
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama8b", "batched", "long", "mha_fp8"])
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "batched", "long", "mha_fp8", "long_fp8"])
 def test_named_workload_full_size(gpu, name):
     case = named_case(name)
     ref, ref_lse = named_reference(name)

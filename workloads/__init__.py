@@ -21,6 +21,11 @@ Workloads (sizes are those of the five named decode cases):
                 (physical block, KV head) equal to amax/448 of that block's
                 valid source values.
 
+Two more workloads share these recipes: ``mha_fp8_kivi`` (the mha_fp8 shape with
+per-channel key and per-token value scales) and ``long_fp8`` (the long shape,
+32768 tokens, with K/V stored as fp8 like mha_fp8 and no append: grouped queries
+over an fp8 pool).
+
 Recipe: q, k, v source values are i.i.d. N(0, 1) float32 rounded to bf16 by
 round-to-nearest-even (for fp8, the float32 values are scaled and encoded
 instead).  Because the values are i.i.d., they are drawn directly in pool
@@ -77,6 +82,8 @@ SPECS = {
                     pool="exact"),
     "mha_fp8_kivi": Spec("mha_fp8_kivi", 5, 4, 40, 40, 128, 16, kv_dtype="fp8_kivi",
                          context=8192, pool="exact"),
+    "long_fp8": Spec("long_fp8", 6, 4, 64, 8, 128, 32, kv_dtype="fp8", context=32768,
+                     pool="oversized2x"),
 }
 
 
