@@ -335,7 +335,6 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   // Matrix path: 16x16x32 bf16 MFMA tiles.  Staged V rows are VSTR elements
   // apart (a shift of 8 banks per row for the transpose reads).
   constexpr int KB = D / 32;                 // k-steps of the score product
-  constexpr int NK = 2 * KB;                 // K loads per chunk (two 16-token tiles)
   constexpr int NN = D / 16;                 // n-tiles of the value product
   constexpr int VSTR = D + 16;
   constexpr int PRS = CT + 4;                // floats per staged weight row
@@ -346,7 +345,6 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   static_assert(BS % TPI == 0 && BS % 16 == 0 && kChunkTokens % CT == 0, "tile geometry");
   static_assert(MFMA || (kWave % M == 0 && PPL * TSTEP * M >= NPAIR && M <= 16), "score mapping");
   static_assert(!MFMA || M <= 16 || M % 16 == 0, "matrix rows come in whole tiles of 16");
-  static_assert(!MFMA || !FP8 || KB % 2 == 0, "fp8 K pieces hold two score steps");
   static_assert(kWaveBytes % 16 == 0, "LDS alignment");
   using Vec = typename KVTraits<FP8>::Vec;
 
@@ -731,14 +729,23 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     float* sm_pw = reinterpret_cast<float*>(sm_wave + CT * VSTR * 2);  // [WR][PRS] weights
     float* sm_alpha = sm_pw + WR * PRS;                                // [WR] rescale factors
 
-    // The product sums over all D dims, so any assignment of dims to (kb, qd,
-    // element) serves, as long as K and q share it.  bf16: step kb, lane group
-    // qd holds dims 32*kb + 8*qd .. +7 (each K row piece is 16 bytes, four lanes
-    // read 64 contiguous bytes of a row).  fp8: dims 64*(kb/2) + 16*qd +
-    // 8*(kb%2) .. +7, so one 16-byte load per lane fetches two steps' codes and
-    // four lanes again read 64 contiguous bytes of a row (with the bf16 mapping
-    // an fp8 row piece would be 8 bytes: twice the cache-line requests per byte).
-    auto kdim = [&](int kb) { return FP8 ? 64 * (kb >> 1) + 16 * qd + 8 * (kb & 1) : 32 * kb + 8 * qd; };
+    // K reaches the A-operand layout one of two ways.  Up to 8 rows per KV head
+    // each lane loads its operand pieces straight from the pool: the product sums
+    // over all D dims, so any assignment of dims to (kb, qd, element) serves if K
+    // and q share it.  bf16: step kb, lane group qd holds dims 32*kb + 8*qd .. +7
+    // (16-byte pieces; four lanes read 64 contiguous bytes of a row).  fp8: dims
+    // 64*(kb/2) + 16*qd + 8*(kb%2) .. +7, so one 16-byte load per lane fetches two
+    // steps' codes and four lanes again read 64 contiguous bytes of a row (with
+    // the bf16 assignment an fp8 piece would be 8 bytes: twice the cache-line
+    // requests per byte, and the 32K G = 8 fp8 step ran 62.9 against 49.5 us).
+    // With 16 rows or more, K rows are loaded whole like V rows and staged through
+    // LDS (STAGE_K, below), with the plain assignment.
+    constexpr bool STAGE_K = M >= 16;
+    constexpr bool FP8_PIECES = FP8 && !STAGE_K;
+    static_assert(!FP8_PIECES || KB % 2 == 0, "fp8 K pieces hold two score steps");
+    auto kdim = [&](int kb) {
+      return FP8_PIECES ? 64 * (kb >> 1) + 16 * qd + 8 * (kb & 1) : 32 * kb + 8 * qd;
+    };
     bf16x8_t qop[RT][KB];                 // q of row 16 rt + hd, dims kdim(kb) .. +7
     int hd_limit[RT], hd_low[RT];         // row 16 rt + hd sees tokens in [low, limit)
 #pragma unroll
@@ -764,14 +771,14 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       for (int n = 0; n < NN; ++n) acc[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // K in the A-operand layout: row (lane & 15) of a 16-token tile, dims
-    // kdim(kb) .. +7 (each instruction reads 16 rows x 64 B: bf16 for one step,
-    // fp8 codes for two, widened to bf16 before the product).  fp8: ks[t16] is
-    // the K scale of the block holding 16-token tile t16 (a block of 16 or 32
-    // tokens holds whole tiles); it multiplies that tile's scores.
-    const uint32_t k_lane_off = (uint32_t)((hd * D + (FP8 ? 16 : 8) * qd) * ESZ);
+    // Direct: row (lane & 15) of a 16-token tile, dims kdim(kb) .. +7 (each
+    // instruction reads 16 rows x 64 B: bf16 for one step, fp8 codes for two,
+    // widened to bf16 before the product).  fp8: ks[t16] is the K scale of the
+    // block holding 16-token tile t16 (a block of 16 or 32 tokens holds whole
+    // tiles); it multiplies that tile's scores.
+    const uint32_t k_lane_off = (uint32_t)((hd * D + (FP8_PIECES ? 16 : 8) * qd) * ESZ);
     using KOp = typename KVTraits<FP8>::Vec;  // 8 elements: uint4 (bf16) or uint2 (fp8)
-    KOp kr[NK];
+    KOp kr[STAGE_K ? 1 : 2 * KB];
     float ks[FP8 ? 2 : 1];
     auto issue_k_with = [&](auto policy, int j) __attribute__((always_inline)) {
       const int t0 = chunk_start(j);
@@ -780,7 +787,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         const int e = CT >= BS ? (16 * t16) / BS : 0;
         const auto rsrc = tile_rsrc(j, e, kbase, true);
         const int first = (t0 + 16 * t16) % BS;
-        if constexpr (FP8) {
+        if constexpr (FP8_PIECES) {
 #pragma unroll
           for (int h = 0; h < KB / 2; ++h) {       // steps 2h and 2h + 1
             const uint4 w = __builtin_bit_cast(
@@ -806,13 +813,26 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       }
     };
     auto issue_k = [&](int j) __attribute__((always_inline)) {
-      if (chunk_streams(j))
-        issue_k_with(StreamPolicy{}, j);
-      else
-        issue_k_with(DefaultPolicy{}, j);
+      if constexpr (!STAGE_K) {
+        if (chunk_streams(j))
+          issue_k_with(StreamPolicy{}, j);
+        else
+          issue_k_with(DefaultPolicy{}, j);
+      }
     };
+    // Staged (STAGE_K): K rows are loaded like V rows (whole rows per instruction,
+    // contiguous), and each chunk's rows pass through the V staging area of LDS
+    // into the A-operand layout.  A paged gather in the direct pattern reads
+    // 5.5-5.8 TB/s against 6.4-6.6 for whole rows; staging adds LDS latency to
+    // each chunk, which pays only where the rows' compute is long anyway (16
+    // rows, 8K: 18.1 -> 17.7 us; 32 rows, 32K: 93.8 -> 92.8) and costs a single
+    // wave per SIMD 0.17 us per chunk at 8 rows.  fp8 codes are widened to bf16
+    // on the way into LDS; ksc[i] is the K scale of row instruction i's block.
+    Vec krow[STAGE_K ? NI : 1];
+    float ksc[STAGE_K ? NI : 1];
     Vec vr[NI];
     float vsc[NI];                           // fp8: V scale of each row instruction's block
+    uint16_t* const sm_k = sm_v;             // K rows share the staging area (K, then V, per chunk)
     const int k4 = hd >> 2, r4 = lane & 3;   // transpose-read source row / column piece
 
     auto run_chunk = [&](int j, auto slow_tag, auto next_tag) {
@@ -822,28 +842,60 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       const int nvalid = s1 - t0;
       f32x4 sc[RT][2];
       float smul[2];                       // score multiplier of each 16-token tile
+      if constexpr (STAGE_K) {
+        // K rows to LDS (rows past the split end hold whatever their slots hold:
+        // their scores are masked by selection below), then the next chunk's K
+        // loads reuse the registers.
 #pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) {
-        bf16x8_t ka[KB];
+        for (int i = 0; i < NI; ++i)
+          *reinterpret_cast<uint4*>(sm_k + (i * TPI + row) * VSTR + 8 * col) =
+              __builtin_bit_cast(uint4, widen_to_bf16x8(krow[i]));
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[kb] = widen_to_bf16x8(kr[t16 * KB + kb]);
+        for (int t16 = 0; t16 < 2; ++t16)
+          smul[t16] = FP8 ? p.scale_log2 * ksc[t16 * (NI / 2)] : p.scale_log2;
+        __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the rows just staged
+        if constexpr (NEXT) {
+          advance_ids(j);
+          issue_rows(j + 1, kbase, krow, ksc, true, true);
+        }
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          sc[rt][t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t16 = 0; t16 < 2; ++t16) {
+          bf16x8_t ka[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
-            sc[rt][t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[rt][kb],
-                                                                 sc[rt][t16], 0, 0, 0);
+            ka[kb] = *reinterpret_cast<const bf16x8_t*>(sm_k + (16 * t16 + hd) * VSTR +
+                                                        32 * kb + 8 * qd);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            sc[rt][t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              sc[rt][t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[rt][kb],
+                                                                   sc[rt][t16], 0, 0, 0);
+          }
         }
-        if constexpr (FP8)
-          smul[t16] = p.scale_log2 * ks[t16];
-        else
-          smul[t16] = p.scale_log2;
-      }
-      __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the operands just used
-      if constexpr (NEXT) {
-        advance_ids(j);
-        issue_k(j + 1);
+      } else {
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16) {
+          bf16x8_t ka[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) ka[kb] = widen_to_bf16x8(kr[t16 * KB + kb]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            sc[rt][t16] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              sc[rt][t16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qop[rt][kb],
+                                                                   sc[rt][t16], 0, 0, 0);
+          }
+          smul[t16] = FP8 ? p.scale_log2 * ks[t16] : p.scale_log2;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the operands just used
+        if constexpr (NEXT) {
+          advance_ids(j);
+          issue_k(j + 1);
+        }
       }
       // This lane's scores: row 16 rt + hd, tokens 16*t16 + 4*qd + r.
       float s[RT][8];
@@ -960,7 +1012,10 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     // Rotating pipeline: K(j+1) is issued right after the scores of chunk j,
     // V(j+1) as soon as V(j) is staged in LDS.
     if (my_n > 0) {
-      issue_k(0);
+      if constexpr (STAGE_K)
+        issue_rows(0, kbase, krow, ksc, true, true);
+      else
+        issue_k(0);
       issue_rows(0, vbase, vr, vsc, false, false);
     }
     for (int j = 0; j + 1 < my_n; ++j) run_chunk(j, std::false_type{}, std::true_type{});
