@@ -644,8 +644,15 @@ def _timed(torch, args, step):
             dist)
 
 
+PROBE_PATTERNS = {0: "whole rows (16 B per lane, 1 KiB contiguous per instruction)",
+                  1: "operand rows: 16 rows x 64 B of 256-byte rows (bf16 K, MFMA layout)",
+                  2: "operand rows: 16 rows x 64 B of 128-byte rows (fp8 K, 16 B per lane)",
+                  3: "operand rows: 16 rows x 32 B of 128-byte rows (fp8 K, 8 B per lane)",
+                  4: "half operand rows (256-byte rows), half whole rows (K and V tiles)"}
+
+
 def probe_rate(args, np, torch, gqa, *, total_bytes, tile_bytes, table, non_temporal,
-               workgroups=None, steps=None):
+               workgroups=None, steps=None, pattern=0):
     """One read-probe configuration: a graph of `steps` launches, each reading
     total_bytes in tiles of tile_bytes (through a random permutation table, or as a
     plain stream), rotated over copies so each launch reads bytes last touched at
@@ -665,7 +672,7 @@ def probe_rate(args, np, torch, gqa, *, total_bytes, tile_bytes, table, non_temp
 
     def step(i):
         gqa.probe_read(base + (i % copies) * ntiles * tile_bytes, ntiles, ids, ntiles,
-                       tile_bytes, non_temporal, workgroups, sink)
+                       tile_bytes, non_temporal, workgroups, sink, pattern=pattern)
 
     sub = argparse.Namespace(**vars(args))
     sub.steps = steps or max(args.steps, 20)
@@ -681,7 +688,7 @@ def probe_rate(args, np, torch, gqa, *, total_bytes, tile_bytes, table, non_temp
             "bytes_per_launch": ntiles * tile_bytes, "tile_bytes": tile_bytes,
             "table": "random permutation" if table else "none (contiguous stream)",
             "non_temporal": bool(non_temporal), "workgroups": workgroups,
-            "launches": sub.steps, "copies_rotated": copies}
+            "launches": sub.steps, "copies_rotated": copies, "pattern": PROBE_PATTERNS[pattern]}
 
 
 def sustained_probe(args, np, torch, gqa, tile_bytes, num_tiles):
@@ -699,7 +706,8 @@ def sustained_probe(args, np, torch, gqa, tile_bytes, num_tiles):
 def probe_suite(args, np, torch, gqa):
     """The read-bandwidth ceilings: a plain streaming read at several sizes, the paged
     gather at each tile size the pools use, and one workgroup gathering alone, each
-    with the non-temporal hint and with the default policy."""
+    with the non-temporal hint and with the default policy; then the paged gather in
+    the per-instruction patterns of the decode kernel's K loads."""
     runs = []
     for size in (32 << 20, 128 << 20, 512 << 20):
         for nt in (1, 0):
@@ -710,6 +718,11 @@ def probe_suite(args, np, torch, gqa):
     for nt in (1, 0):
         runs.append(dict(total_bytes=8 << 20, tile_bytes=4096, table=True, non_temporal=nt,
                          workgroups=1, steps=5))
+    # the decode kernel's per-instruction patterns of K loads, with its hint
+    for pattern, tile in ((1, 4096), (1, 8192), (4, 8192), (2, 2048), (2, 4096), (3, 2048),
+                          (3, 4096)):
+        runs.append(dict(total_bytes=512 << 20, tile_bytes=tile, table=True, non_temporal=1,
+                         pattern=pattern))
     out = []
     for kw in runs:
         r = probe_rate(args, np, torch, gqa, **kw)

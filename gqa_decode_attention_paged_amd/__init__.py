@@ -111,6 +111,9 @@ def load():
     lib.gqa_probe_read.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.gqa_probe_read.restype = ctypes.c_int
+    lib.gqa_probe_read_pattern.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.gqa_probe_read_pattern.restype = ctypes.c_int
     lib.gqa_workspace_read_status.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_uint32), _P]
     lib.gqa_workspace_read_status.restype = ctypes.c_int
@@ -543,11 +546,20 @@ def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, k_scale=None, v_sca
                                      _stream(k_cache)))
 
 
+# Per-instruction load patterns of the read probe (include/gqa_probe.h).
+PROBE_WHOLE_ROWS = 0
+PROBE_OPERAND_ROWS_256 = 1
+PROBE_OPERAND_ROWS_128 = 2
+PROBE_OPERAND_ROWS_128_NARROW = 3
+PROBE_MIXED_256 = 4
+
+
 def probe_read(pool_address, pool_tiles, tile_ids, num_tiles, tile_bytes, non_temporal,
-               num_workgroups, sink):
+               num_workgroups, sink, pattern=PROBE_WHOLE_ROWS):
     """One read-probe launch (measurement only): num_tiles tiles of tile_bytes bytes from
     the device buffer at pool_address (an address inside a tensor the caller keeps,
-    holding pool_tiles tiles), through tile_ids (int32 [num_tiles]) or contiguously."""
+    holding pool_tiles tiles), through tile_ids (int32 [num_tiles]) or contiguously,
+    each wave instruction covering a tile as `pattern` (PROBE_*) says."""
     chk = _Checks()
     if tile_ids is not None:
         chk(tile_ids, "tile_ids", "i32", min_rows=num_tiles)
@@ -555,10 +567,10 @@ def probe_read(pool_address, pool_tiles, tile_ids, num_tiles, tile_bytes, non_te
     if sink.dtype not in (__import__("torch").int32, __import__("torch").uint32):
         raise TypeError("sink: expected int32 or uint32")
     chk.on_gpu()
-    _check(load().gqa_probe_read(ctypes.c_void_p(int(pool_address)), int(pool_tiles),
-                                 _ptr(tile_ids), int(num_tiles), int(tile_bytes),
-                                 1 if non_temporal else 0, int(num_workgroups), _ptr(sink),
-                                 _stream(sink)))
+    _check(load().gqa_probe_read_pattern(ctypes.c_void_p(int(pool_address)), int(pool_tiles),
+                                         _ptr(tile_ids), int(num_tiles), int(tile_bytes),
+                                         int(pattern), 1 if non_temporal else 0,
+                                         int(num_workgroups), _ptr(sink), _stream(sink)))
 
 
 def kv_gather(cache, block_tables, seq, num_tokens):

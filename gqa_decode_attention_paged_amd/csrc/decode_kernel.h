@@ -823,7 +823,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     // Staged (STAGE_K): K rows are loaded like V rows (whole rows per instruction,
     // contiguous), and each chunk's rows pass through the V staging area of LDS
     // into the A-operand layout.  A paged gather in the direct pattern reads
-    // 5.5-5.8 TB/s against 6.4-6.6 for whole rows; staging adds LDS latency to
+    // 5.6-5.8 TB/s against 6.6-6.7 for whole rows; staging adds LDS latency to
     // each chunk, which pays only where the rows' compute is long anyway (16
     // rows, 8K: 18.1 -> 17.7 us; 32 rows, 32K: 93.8 -> 92.8) and costs a single
     // wave per SIMD 0.17 us per chunk at 8 rows.  fp8 codes are widened to bf16

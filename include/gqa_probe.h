@@ -49,6 +49,41 @@ gqa_status gqa_probe_read(const void* pool, int64_t pool_tiles, const int32_t* t
                           int64_t num_tiles, int32_t tile_bytes, int32_t non_temporal,
                           int32_t num_workgroups, uint32_t* sink, hipStream_t stream);
 
+/*
+ * Per-instruction load patterns: how the 64 lanes of one wave load instruction
+ * cover a tile, in the ways the decode kernel reads its tiles.  Every pattern
+ * reads each 32-bit word of a tile exactly once.
+ */
+enum {
+  GQA_PROBE_WHOLE_ROWS = 0,           /* 16 B per lane, 1 KiB contiguous per
+                                         instruction (V rows; K rows on the vector
+                                         path, and on the matrix path at 16 rows
+                                         or more) */
+  GQA_PROBE_OPERAND_ROWS_256 = 1,     /* 16 rows x 64 B of 256-byte rows, 16 B per
+                                         lane: bf16 K (d_h 128) loaded straight
+                                         into the MFMA operand layout */
+  GQA_PROBE_OPERAND_ROWS_128 = 2,     /* 16 rows x 64 B of 128-byte rows, 16 B per
+                                         lane: fp8 K (d_h 128) in the operand
+                                         layout, two score steps per lane */
+  GQA_PROBE_OPERAND_ROWS_128_NARROW = 3,  /* 16 rows x 32 B of 128-byte rows, 8 B per
+                                         lane: fp8 K with one score step per lane */
+  GQA_PROBE_MIXED_256 = 4             /* even table entries as OPERAND_ROWS_256,
+                                         odd ones as WHOLE_ROWS: the K and V tiles
+                                         of a bf16 step */
+};
+
+/*
+ * gqa_probe_read_pattern — gqa_probe_read with the per-instruction load
+ * pattern `pattern` (GQA_PROBE_*); gqa_probe_read is GQA_PROBE_WHOLE_ROWS.
+ * tile_bytes must be a multiple of 4096 for OPERAND_ROWS_256 and MIXED_256
+ * and of 2048 for the 128-byte-row patterns; other sizes and patterns return
+ * GQA_ERR_UNSUPPORTED.  Arguments and errors are otherwise gqa_probe_read's.
+ */
+gqa_status gqa_probe_read_pattern(const void* pool, int64_t pool_tiles, const int32_t* tile_ids,
+                                  int64_t num_tiles, int32_t tile_bytes, int32_t pattern,
+                                  int32_t non_temporal, int32_t num_workgroups, uint32_t* sink,
+                                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

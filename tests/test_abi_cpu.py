@@ -169,6 +169,18 @@ def test_probe_validation(lib):
     assert pr(P(16), 8, None, 0, 4096, 1, 1, P(16), None) == 0          # nothing to read
 
 
+def test_probe_pattern_validation(lib):
+    P = ctypes.c_void_p
+    pp = lib.gqa_probe_read_pattern
+    call = lambda tile, pattern, pool=P(16): pp(pool, 8, None, 8, tile, pattern, 1, 1, P(16), None)
+    assert call(4096, 5) == 2 and call(4096, -1) == 2                   # no such pattern
+    assert call(2048, 1) == 2 and call(2048, 4) == 2                    # 256-byte rows: 4 KiB tiles
+    assert call(1024, 2) == 2 and call(1024, 3) == 2                    # 128-byte rows: 2 KiB tiles
+    for tile, pattern in ((1024, 0), (4096, 1), (2048, 2), (2048, 3), (8192, 4)):
+        assert call(tile, pattern, None) == 1                           # accepted; NULL pool refused
+        assert pp(P(16), 8, None, 0, tile, pattern, 1, 1, P(16), None) == 0   # nothing to read
+
+
 def test_read_status_validation(lib):
     P = ctypes.c_void_p
     word = ctypes.c_uint32(7)
