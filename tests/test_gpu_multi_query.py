@@ -217,3 +217,51 @@ def test_fused_verify_step_matches_two_calls_bitwise(gpu, hq, hkv, nq, bs):
     assert torch.equal(bits(d1["k_cache"]), bits(d2["k_cache"]))
     assert torch.equal(bits(d1["v_cache"]), bits(d2["v_cache"]))
     assert_parity(o2, l2, ref, ref_lse, "fused verify")
+
+
+@pytest.mark.parametrize("hq,hkv,nq", [(32, 8, 4), (64, 8, 4)])
+def test_unused_block_scales_are_never_used_staged(gpu, hq, hkv, nq):
+    """Regression for the variants that stage K through LDS (16 and 32 rows, fp8):
+    whole blocks past a split's end read block 0 as a stand-in, and its K scale
+    multiplies the scores of a masked tile.  Block 0 is made unused here with NaN
+    scales; the outputs must still match the oracle, which never reads it."""
+    lens = [48, 1000, 2064, 7]
+    spec = small_spec(num_seqs=4, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=16,
+                      kv_dtype="fp8", context=2064, pool="oversized2x", case_id=7900 + hq)
+    case = make_multi_query_case(spec, nq, seed=3, context_lens=lens, append=False)
+    tab = case["block_tables"]
+    used = set(int(x) for x in tab.ravel() if x >= 0)
+    u = next(i for i in range(case["k_pool"].shape[0]) if i not in used)
+    # without an append the pool before and after it is one array: swap each once
+    arrays = {id(case[key]): case[key] for key in
+              ("k_pool", "v_pool", "k_pool_full", "v_pool_full", "k_scale", "v_scale")}
+    for a in arrays.values():
+        a[[0, u]] = a[[u, 0]]
+    tab[tab == 0] = u
+    assert 0 not in set(int(x) for x in tab.ravel())
+    case["k_scale"][0] = np.nan
+    case["v_scale"][0] = np.nan
+    ref, ref_lse = _reference(case)
+    out, lse = _verify_step(gpu, case, to_device(case))
+    assert_parity(out, lse, ref, ref_lse, f"NaN scales in unused block 0, {hq // hkv * nq} rows")
+
+
+def test_split_length_override_multi_query_fp8(gpu):
+    """The split-length override on the staged fp8 path (16 rows): parity, and the
+    same bits for a sequence alone and in the batch."""
+    spec = small_spec(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      kv_dtype="fp8", context=3000, case_id=7950)
+    case = make_multi_query_case(spec, 4, seed=5, context_lens=[4, 700, 3000, 1500],
+                                 append=False)
+    ref, ref_lse = _reference(case)
+    try:
+        gpu.set_split_tokens(256)
+        out, lse = _verify_step(gpu, case, to_device(case), max_context_len=3000)
+        one = dict(case)
+        for key in ("q", "block_tables", "context_lens", "positions"):
+            one[key] = case[key][2:3]
+        o1, l1 = _verify_step(gpu, one, to_device(one))
+    finally:
+        gpu.set_split_tokens(0)
+    assert_parity(out, lse, ref, ref_lse, "split length 256, fp8, 16 rows")
+    assert np.array_equal(o1[0], out[2]) and np.array_equal(l1[0], lse[2])
