@@ -532,10 +532,14 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   const int s0 = base + split * plan.split_tokens;
   const int s1 = min(ctx, s0 + plan.split_tokens);
   const int my_n = wave_chunks(s0, s1);
+  int append_j = -1;                         // bf16 append: this wave's chunk holding a new row
   // Fused append: the token at `pos`, or with append_tail the Q query positions
   // ctx-Q .. ctx-1 (row i of k_new/v_new).  The wave whose chunk holds a new
-  // token commits its K/V rows and waits for the stores, so its loads then read
-  // the token back from the cache.  fp8 pools: the wave whose chunk holds a
+  // token commits its K/V rows and waits for the stores before it issues that
+  // chunk's loads, so they read the token back from the cache (bf16: append_j
+  // is that chunk's index among the wave's chunks; the wait sits where its loads
+  // are issued, and by then the stores have long completed: 8K step 13.33 ->
+  // 13.19 us).  fp8 pools: the wave whose chunk holds a
   // block's first new token quantises that block's new rows (the append policy
   // of wave_append_fp8: its scale may grow and its older codes be re-encoded),
   // waits for the stores and invalidates the CU's vector L1, so every later
@@ -574,13 +578,15 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       if (any_here) __syncthreads();                       // uniform over the workgroup
     }
   } else {
+    // bf16: a new row is read back only by the wave whose chunk holds it, so
+    // that wave waits for its stores just before it issues that chunk's loads
+    // (append_j, below), not before its first loads.
     const int na = p.append_tail ? Q : (pos >= 0 ? 1 : 0);
     const int a0 = p.append_tail ? ctx - Q : pos;
-    bool wrote = false;
     for (int i = 0; i < na; ++i) {
       const int ap = a0 + i;
       if (ap < s0 || ap >= s1 || ((ap - s0) / CT) % WAVES != wave) continue;
-      wrote = true;
+      append_j = (ap - s0) / CT / WAVES;                 // this wave's chunk holding the row
       if (row != 0) continue;
       const size_t src = (((size_t)b * (p.append_tail ? Q : 1) + i) * p.num_kv_heads + kvh) * D +
                          col * 8;
@@ -595,7 +601,6 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         raise_status(p.status, GQA_STATUS_BAD_APPEND);
       }
     }
-    if (wrote) wait_vector_memory();
   }
   if (b != (int)blockIdx.z || s0 != hs0 || s1 != hs1)
     ids = load_ids(s0, s1, my_n, 0);               // the speculation did not apply
@@ -856,6 +861,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the rows just staged
         if constexpr (NEXT) {
           advance_ids(j);
+          if (j + 1 == append_j) wait_vector_memory();   // the new row is in chunk j+1
           issue_rows(j + 1, kbase, krow, ksc, true, true);
         }
         __builtin_amdgcn_wave_barrier();
@@ -894,6 +900,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
         __builtin_amdgcn_sched_barrier(0);   // K(j+1) overwrites the operands just used
         if constexpr (NEXT) {
           advance_ids(j);
+          if (j + 1 == append_j) wait_vector_memory();   // the new row is in chunk j+1
           issue_k(j + 1);
         }
       }
@@ -1012,6 +1019,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     // Rotating pipeline: K(j+1) is issued right after the scores of chunk j,
     // V(j+1) as soon as V(j) is staged in LDS.
     if (my_n > 0) {
+      if (append_j == 0) wait_vector_memory();           // the new row is in chunk 0
       if constexpr (STAGE_K)
         issue_rows(0, kbase, krow, ksc, true, true);
       else
@@ -1149,6 +1157,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       __builtin_amdgcn_sched_barrier(0);   // keep K(j+1) behind the scores of chunk j
       if constexpr (NEXT) {
         advance_ids(j);
+        if (j + 1 == append_j) wait_vector_memory();     // the new row is in chunk j+1
         issue_rows_with(policy, j + 1, kbase, kr, ks, true, true);
       }
       __builtin_amdgcn_wave_barrier();
@@ -1235,6 +1244,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     // j, V(j+1) right after its value sums, so the next chunk's loads fly during
     // compute with no extra registers.
     if (my_n > 0) {
+      if (append_j == 0) wait_vector_memory();           // the new row is in chunk 0
       issue_rows(0, kbase, kr, ks, true, true);
       issue_rows(0, vbase, vr, vs, false, false);
     }
