@@ -90,7 +90,6 @@ struct DecodeParams {
   int32_t num_blocks;
   int32_t max_splits;           // row stride of the split partials
   int32_t proportional;         // slots shared out by sequence length (2 <= B <= 64)
-  int32_t min_split_tokens;     // shortest split the plan makes (kMinSplitTokens, or an override)
   float scale_log2;             // softmax_scale * log2(e)
 };
 
@@ -304,6 +303,10 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   constexpr bool FP8 = KV != 0;
   const int target_splits = plan_flags & 0xff;
   const int Q = (plan_flags >> 16) & 0xff;   // query positions per sequence
+  // Shortest split: kMinSplitTokens, or a split-length override T (T / 32 in bits
+  // 9-15 and 24-31), from the preloaded word so the plan below waits for nothing.
+  const int split32 = (int)((((uint32_t)plan_flags >> 9) & 0x7fu) | (((uint32_t)plan_flags >> 24) << 7));
+  const int min_split_tokens = split32 ? split32 * kChunkTokens : kMinSplitTokens;
   constexpr bool KIVI = KV == 2;
   // M is the row capacity: the rows of one (sequence, KV head) are its query
   // positions times its G query heads, row m = i*G + g (R = G*Q <= M of them).
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     return first > 0 ? first / BS * BS : 0;
   };
   const int hbase = span_base(hint_ctx);
-  const SplitPlan hplan = split_plan(hint_ctx - hbase, target_splits, p.min_split_tokens);
+  const SplitPlan hplan = split_plan(hint_ctx - hbase, target_splits, min_split_tokens);
   const int hs0 = hbase + (int)blockIdx.x * hplan.split_tokens;
   const int hs1 = min(hint_ctx, hs0 + hplan.split_tokens);
   const int hmy_n = (int)blockIdx.x < hplan.num_splits ? wave_chunks(hs0, hs1) : 0;
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   const bool ctx_bad = ctx < 0 || ctx > max_blocks * BS || (ctx > 0 && ctx < Q);
   const int base = ctx_bad ? 0 : span_base(ctx);    // first token of the attended span
   const SplitPlan plan = split_plan(ctx_bad ? 0 : ctx - base,
-                                    proportional ? slots_b : target_splits, p.min_split_tokens);
+                                    proportional ? slots_b : target_splits, min_split_tokens);
   // Whatever the plan, the last 15% of a split's tokens take the default policy
   // too: a mix of the two policies reads faster than either alone (32K step
   // 87.7 -> 85.9 us, 8K 14.15 -> 13.78 us; 0.75 and 0.9 measure slower).

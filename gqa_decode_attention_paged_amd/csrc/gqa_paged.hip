@@ -220,7 +220,7 @@ int rounds_override() {
 // 0, or the shortest split in tokens, a multiple of kChunkTokens in
 // [kMinSplitTokens, kMaxSplitTokensOverride].  When set, every attention call
 // takes the batch-invariant plan with that minimum in place of kMinSplitTokens.
-constexpr int kMaxSplitTokensOverride = 1 << 20;
+constexpr int kMaxSplitTokensOverride = 1 << 19;   // T / 32 fits the kernel's 15 plan bits
 bool valid_split_tokens(int t) {
   return t >= gqa::kMinSplitTokens && t <= kMaxSplitTokensOverride && t % gqa::kChunkTokens == 0;
 }
@@ -550,7 +550,6 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   p.num_blocks = s->num_blocks;
   p.max_splits = ws_splits;
   p.proportional = proportional ? 1 : 0;
-  p.min_split_tokens = min_tokens;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   // The leading scalar arguments of paged_decode_kernel (preloaded into SGPRs).
   const int32_t* bt_arg = block_tables;
@@ -558,7 +557,12 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
   int32_t hint_arg = max_context_len;
   int32_t max_blocks_arg = s->max_blocks_per_seq;
   int32_t window_arg = s->sliding_window;
-  int32_t plan_arg = target | (proportional ? 1 << 8 : 0) | num_queries << 16;
+  // bits 0-7 split target, 8 proportional sharing, 16-23 query positions; the
+  // split-length override T as T / 32 in bits 9-15 (low) and 24-31 (high), 0 if none
+  const uint32_t split32 = split_tokens > 0 ? (uint32_t)split_tokens / gqa::kChunkTokens : 0u;
+  int32_t plan_arg = (int32_t)((uint32_t)target | (proportional ? 1u << 8 : 0u) |
+                               ((split32 & 0x7fu) << 9) | ((uint32_t)num_queries << 16) |
+                               ((split32 >> 7) << 24));
   if (clear_counters) {
     // A shared workspace (the static scratch): zero its arrival counters and status
     // word with a fill kernel on the same stream, after every argument was checked.

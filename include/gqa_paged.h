@@ -68,7 +68,7 @@
  *    Unset, the library chooses; neither applies under GQA_FLAG_BATCH_INVARIANT.
  *    Like any split plan they change results in the last bits only.
  *  - Split-length override: GQA_SPLIT_TOKENS (read once per process, or set at
- *    run time with gqa_set_split_tokens) = T, a multiple of 32 in [128, 2^20].
+ *    run time with gqa_set_split_tokens) = T, a multiple of 32 in [128, 2^19].
  *    When set, every attention call splits each sequence by its own length
  *    with splits of at least T tokens (at most 64 of them), as under
  *    GQA_FLAG_BATCH_INVARIANT with T in place of 128: results stay
@@ -202,7 +202,7 @@ gqa_status gqa_kv_append_tokens(const gqa_paged_shape* shape, int32_t num_tokens
 int32_t gqa_decode_num_splits(int32_t context_len);
 
 /*
- * gqa_set_split_tokens — set (tokens = T, a multiple of 32 in [128, 2^20]) or
+ * gqa_set_split_tokens — set (tokens = T, a multiple of 32 in [128, 2^19]) or
  * clear (tokens = 0) the process-wide split-length override that
  * GQA_SPLIT_TOKENS sets at start-up.  Calls made after it returns use the new
  * value; a call already being launched on another thread may use either.

@@ -311,13 +311,13 @@ def test_split_tokens_override(lib):
     import gqa_decode_attention_paged_amd as gqa
     assert gqa.split_tokens() == 0
     try:
-        for t in (128, 160, 2080, 1 << 20):
+        for t in (128, 160, 2080, 4128, 1 << 19):
             gqa.set_split_tokens(t)
             assert gqa.split_tokens() == t
             for ctx in list(range(0, 700, 7)) + [2047, 2048, 2049, 8192, 32769, 1 << 22]:
                 assert gqa.num_splits(ctx) == _split_plan(ctx, 64, t)[0], (t, ctx)
         gqa.set_split_tokens(2080)
-        for bad in (-32, 1, 96, 127, 130, 2081, (1 << 20) + 32, 1 << 21):
+        for bad in (-32, 1, 96, 127, 130, 2081, (1 << 19) + 32, 1 << 20):
             with pytest.raises(gqa.GqaError):
                 gqa.set_split_tokens(bad)
             assert gqa.split_tokens() == 2080

@@ -77,7 +77,7 @@ def split_override(gpu):
     gpu.set_split_tokens(0)
 
 
-@pytest.mark.parametrize("tokens", [256, 1024])
+@pytest.mark.parametrize("tokens", [256, 1024, 4128])   # 4128: T / 32 needs the high plan bits
 def test_split_length_override_is_batch_invariant(split_override, tokens):
     """With a split-length override the results match the oracle, and a sequence
     gives the same bits alone (small hint) and in the batch (large hint)."""
