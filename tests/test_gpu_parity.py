@@ -224,10 +224,13 @@ def test_fused_append_attention_full_size(gpu, name):
     assert np.array_equal(k, case["k_pool_full"]) and np.array_equal(v, case["v_pool_full"])
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (8, 8), (64, 8)])   # matrix G=4, vector G=1, G=8
 @pytest.mark.parametrize("ctx", [1, 17, 129, 700, 4097])
-def test_fused_append_matches_two_calls_bitwise(gpu, ctx):
-    spec = small_spec(num_seqs=3, num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
-                      context=ctx, append=True, case_id=2700 + ctx)
+def test_fused_append_matches_two_calls_bitwise(gpu, ctx, hq, hkv):
+    """The fused step equals the append followed by attention, bit for bit: the new
+    row sits in a wave's first chunk (ctx 1, 17) or in a later one."""
+    spec = small_spec(num_seqs=3, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=16,
+                      context=ctx, append=True, case_id=2700 + ctx + hq)
     case = make_case(spec, seed=9)
     o1, l1 = run_step(gpu, to_device(case), case)
     o2, l2 = run_fused_step(gpu, to_device(case), case)
