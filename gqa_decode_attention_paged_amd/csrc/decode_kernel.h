@@ -1327,7 +1327,11 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       // A row may see none of this split's tokens (a query position before the
       // split's start): its weight in the final merge is 2^-inf = 0, and its
       // partial is 0 rather than 0/0, which would poison that merge.
-      const f32x4 o = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
+      // Scaling by 1/L, or by 0 (O is then 0: every weight of the row is 0), keeps
+      // the LDS reads of the waves' sums out of a branch behind the weights, and
+      // takes one divide instead of four.
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const f32x4 o = O * inv;
       const float lse2 = any_bad ? __builtin_nanf("") : mx + log2f(L);
       if (nsplit == 1) {
         const float nan = __builtin_nanf("");
@@ -1355,7 +1359,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
       L = fmaf(a, sm_l[w][g], L);
       O = fmaf(a, sm_acc(w, g, d), O);
     }
-    const float o = L > 0.f ? O / L : 0.f;         // a row with no token here: 0, not 0/0
+    const float o = O * (L > 0.f ? 1.f / L : 0.f);  // a row with no token here: 0, not 0/0
     const float lse2 = any_bad ? __builtin_nanf("") : mx + log2f(L);
     if (nsplit == 1) {
       p.out[row_index(g) * D + d] = any_bad ? __builtin_nanf("") : o;
