@@ -90,8 +90,14 @@ struct DecodeParams {
   int32_t num_blocks;
   int32_t max_splits;           // row stride of the split partials
   int32_t proportional;         // slots shared out by sequence length (2 <= B <= 64)
+  int32_t defer_merge;          // 1: publish the partials only; merge_splits_kernel merges
   float scale_log2;             // softmax_scale * log2(e)
 };
+
+// Word of each (sequence, KV head) counter line that holds its split count when
+// the merge is deferred to merge_splits_kernel (word 0 is the arrival counter;
+// the first line's word 1 is the status word).
+constexpr int kSplitCountWord = 2;
 
 constexpr float kLazyLog2 = 8.0f;
 // Arrival counters sit 256 B apart: the splits of every (sequence, KV head)
@@ -520,8 +526,10 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
     }
   }
 
+  const size_t pair_line = ((size_t)b * p.num_kv_heads + kvh) * kCounterStride;
   if (degenerate) {
     if (split != 0) return;
+    if (p.defer_merge && tid == 0) p.counters[pair_line + kSplitCountWord] = 0;  // written here
     const bool bad = ctx_bad || too_long;
     if (tid == 0 && bad)
       raise_status(p.status, ctx_bad ? GQA_STATUS_BAD_CONTEXT_LEN : GQA_STATUS_CONTEXT_OVER_HINT);
@@ -532,6 +540,8 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   }
   const int nsplit = plan.num_splits;
   if (split >= nsplit) return;
+  if (p.defer_merge && split == 0 && tid == 0)
+    p.counters[pair_line + kSplitCountWord] = (uint32_t)nsplit;
   const int s0 = base + split * plan.split_tokens;
   const int s1 = min(ctx, s0 + plan.split_tokens);
   const int my_n = wave_chunks(s0, s1);
@@ -1371,6 +1381,7 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   }
   }
   if (nsplit == 1) return;
+  if (p.defer_merge) return;                     // merge_splits_kernel merges after this launch
 
   // Publish, count arrivals; the last workgroup of this (sequence, KV head) merges.
   wait_vector_memory();
@@ -1478,6 +1489,72 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
   if (tid == 0)
     __hip_atomic_store(&p.counters[((size_t)b * p.num_kv_heads + kvh) * kCounterStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Deferred final merge (the decode launch ran with defer_merge): one wave per
+// (row, KV head, sequence), spread over the GPU instead of one workgroup per
+// (sequence, KV head).  The split count comes from the decode launch
+// (kSplitCountWord); with fewer than two splits that launch wrote the outputs
+// itself.  The weights are the log-sum-exp merge of the splits' base-2 lse; lane
+// s loads split s's lse, and the float4 columns of the row are shared out over
+// LG lane groups, each taking every LG-th split, so all loads fly together.
+// Merges splits in the order s = 0, 1, ... within a lane group, then adds the
+// groups' sums.
+template <int D>
+__global__ __launch_bounds__(kWave) void merge_splits_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    const uint32_t* __restrict__ counters, int32_t num_kv_heads, int32_t M, int32_t max_splits,
+    int32_t Q, int32_t num_q_heads, int32_t G, int32_t group_shift, float* __restrict__ out,
+    float* __restrict__ out_lse) {
+  constexpr int C4 = D / 4;                        // float4 columns of a row
+  constexpr int LG = kWave / C4;                   // lane groups
+  constexpr int PER = kMaxSplits / LG;             // splits per lane group, at most
+  const int g = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const size_t pair = (size_t)b * num_kv_heads + kvh;
+  const int nsplit = (int)counters[pair * kCounterStride + kSplitCountWord];
+  if (nsplit < 2) return;
+  const size_t prow = pair * max_splits;
+  const int col = lane % C4, grp = lane / C4;
+  const float x = lane < nsplit ? ws_lse[(prow + lane) * M + g] : kNegInf;
+  f32x4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int si = grp + u * LG;
+    v[u] = si < nsplit ? *reinterpret_cast<const f32x4*>(ws_o + ((prow + si) * M + g) * D + 4 * col)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bool nan = __any(x != x);
+  float mx = x;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+  const float w = lane < nsplit ? fast_exp2(x - mx) : 0.f;
+  float L = w;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m, kWave);
+  const float wn = w / L;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int si = grp + u * LG;
+    const float ws = __shfl(wn, si < kWave ? si : 0, kWave);
+    if (si < nsplit) {
+      o.x = fmaf(ws, v[u].x, o.x); o.y = fmaf(ws, v[u].y, o.y);
+      o.z = fmaf(ws, v[u].z, o.z); o.w = fmaf(ws, v[u].w, o.w);
+    }
+  }
+#pragma unroll
+  for (int m = C4; m < kWave; m <<= 1) {
+    o.x += __shfl_xor(o.x, m, kWave); o.y += __shfl_xor(o.y, m, kWave);
+    o.z += __shfl_xor(o.z, m, kWave); o.w += __shfl_xor(o.w, m, kWave);
+  }
+  // row g is query g / G of head kvh * G + g % G
+  const size_t row = ((size_t)b * Q + (g >> group_shift)) * num_q_heads + kvh * G + (g & (G - 1));
+  if (grp == 0) {
+    const float nanf = __builtin_nanf("");
+    *reinterpret_cast<f32x4*>(out + row * D + 4 * col) = nan ? f32x4{nanf, nanf, nanf, nanf} : o;
+  }
+  if (out_lse && lane == 0) out_lse[row] = nan ? __builtin_nanf("") : (mx + log2f(L)) * kLn2;
 }
 
 // Zero the arrival counters of a workspace (used once, before its first call).

@@ -67,6 +67,10 @@
  *    split target for r rounds of the GPU's resident workgroups instead of one).
  *    Unset, the library chooses; neither applies under GQA_FLAG_BATCH_INVARIANT.
  *    Like any split plan they change results in the last bits only.
+ *    GQA_DEFER_MERGE = 1 merges the context splits in a second kernel launch (on
+ *    the same stream), 2 in the attention launch itself; unset, calls with 16 or
+ *    more query rows per KV head use the second launch.  The merge arithmetic is
+ *    the same either way; its summation order differs.
  *  - Split-length override: GQA_SPLIT_TOKENS (read once per process, or set at
  *    run time with gqa_set_split_tokens) = T, a multiple of 32 in [128, 2^19].
  *    When set, every attention call splits each sequence by its own length
