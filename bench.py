@@ -68,6 +68,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 ROTATE_BYTES = 1 << 30         # distance between reuses of one pool copy
 COPY_BYTES = 256 << 20         # read and written by the PMC calibration kernel
 METRIC = "decode-attention KV-read HBM GB/s (% of MI355X peak) and µs/step"
+MERGE_KERNEL = "merge_splits_kernel"    # the split merge's own launch (16 or more rows)
 DEFAULT_WORKLOAD = "long"
 
 # Figures the pages quote for other hardware: context only, neither target nor
@@ -201,14 +202,28 @@ def write_kernel_time(workload, trace_dir, kv_bytes):
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
-    durs = []
+    # A call whose split merge runs in its own launch (merge_splits_kernel) lasts
+    # from its decode dispatch's start to the end of the merge dispatch that follows.
+    events = []
     for path in files:
         with open(path) as f:
             for row in csv.DictReader(f):
-                if kname in row["Kernel_Name"]:
-                    durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+                n = row["Kernel_Name"]
+                if kname in n or MERGE_KERNEL in n:
+                    events.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]),
+                                   MERGE_KERNEL in n))
+    events.sort()
+    durs, merged = [], False
+    for i, (start, end, is_merge) in enumerate(events):
+        if is_merge:
+            continue
+        if i + 1 < len(events) and events[i + 1][2]:
+            end, merged = events[i + 1][1], True
+        durs.append((end - start) / 1e3)
     if not durs:
         raise SystemExit(f"no {kname} dispatches in {files}")
+    if merged:
+        kname = f"{kname} + {MERGE_KERNEL}"
     durs.sort()
     q = lambda f: durs[min(len(durs) - 1, int(f * len(durs)))]
     out = {"workload": workload, "kernel": kname, "kernel_source_sha": kernel_source_hash(),
@@ -266,20 +281,26 @@ def write_traffic(workload, pmc_dir, kv_bytes):
     import statistics
     kname = "kv_copy_blocks_kernel" if workload == "cow_fork" else "paged_decode_kernel"
     is_decode = lambda n: kname in n
+    is_merge = lambda n: MERGE_KERNEL in n
     is_copy = lambda n: "elementwise" in n and "Fill" not in n
     out = {"workload": workload, "kernel_source_sha": kernel_source_hash(),
            "algorithmic_bytes_per_call": kv_bytes}
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         cal, _ = _pmc_per_dispatch(os.path.join(pmc_dir, "copy_" + sub), counter, is_copy)
         run, _ = _pmc_per_dispatch(os.path.join(pmc_dir, sub), counter, is_decode)
+        mrg, _ = _pmc_per_dispatch(os.path.join(pmc_dir, sub), counter, is_merge)
         if not cal or not run:
             raise SystemExit(f"{counter}: missing dispatches (copy {len(cal)}, decode {len(run)})")
         cal_kib = statistics.median(cal.values())
         scale = COPY_BYTES / (cal_kib * 1024.0)
         kib = statistics.median(run.values())
         out[counter] = {"decode_kib_median": kib, "decode_dispatches": len(run),
-                        "copy_kib_median": cal_kib, "copy_dispatches": len(cal),
-                        "scale": scale, "bytes_per_call": kib * 1024.0 * scale}
+                        "copy_kib_median": cal_kib, "copy_dispatches": len(cal), "scale": scale}
+        if mrg:                    # the split merge's own launch, one per call
+            out[counter]["merge_kib_median"] = statistics.median(mrg.values())
+            out[counter]["merge_dispatches"] = len(mrg)
+            kib += out[counter]["merge_kib_median"]
+        out[counter]["bytes_per_call"] = kib * 1024.0 * scale
     out["hbm_bytes_per_call"] = round(out["FETCH_SIZE"]["bytes_per_call"] +
                                       out["WRITE_SIZE"]["bytes_per_call"])
     out["traffic_over_algorithmic"] = out["hbm_bytes_per_call"] / kv_bytes
@@ -509,7 +530,8 @@ def main():
                   "policy + split attention + log-sum-exp merge)")
     elif verify:
         kernel = ("paged_decode_kernel (fused 4-token KV append + 4 query positions, split "
-                  "attention + log-sum-exp merge)")
+                  "attention) + merge_splits_kernel (log-sum-exp merge of the splits, its own "
+                  "launch at 16 or more rows per KV head)")
     elif k_new is not None:
         kernel = "paged_decode_kernel (fused KV append + split attention + log-sum-exp merge)"
     elif spec.kv_dtype == "fp8_kivi":
