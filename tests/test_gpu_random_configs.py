@@ -1,0 +1,88 @@
+"""Seeded random configurations against the float64 oracle.
+
+Each case draws a combination the other tests cover one axis at a time: head
+dim, block size, grouping G, query positions Q, KV dtype (bf16, fp8 with block
+scales, fp8 KIVI), sliding window, batch size with ragged (and empty) lengths,
+pool placement, split plan (default, batch-invariant flag, split-length
+override) and, for bf16, the fused append.  Sizes stay small enough for the
+oracle; rows per KV head stay within the library's limits (G*Q <= 32, <= 8 for
+KIVI), and lengths are 0 or at least Q (0 < ctx < Q is malformed by definition).
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests._dev import to_device, assert_parity
+from tests.test_gpu_window import _ref, _run
+from workloads import make_case, make_multi_query_case, small_spec
+
+pytestmark = pytest.mark.gpu
+CASES = 96
+
+
+def _draw(i):
+    rng = np.random.default_rng([2024, 12, i])
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    dt = str(rng.choice(["bf16", "bf16", "fp8", "fp8_kivi"]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    cap = 8 if dt == "fp8_kivi" else 32
+    nq = min(int(rng.choice([1, 1, 1, 2, 3, 4, 8])), cap // g)
+    b = int(rng.integers(1, 7))
+    lens = rng.integers(nq, 2600, b)
+    lens[rng.random(b) < 0.1] = 0                     # an empty sequence now and then
+    window = 0 if rng.random() < 0.6 else int(rng.integers(1, 1500))
+    plan = str(rng.choice(["default", "default", "invariant", "override"]))
+    tokens = int(rng.choice([128, 256, 512, 1024, 4128]))
+    fused = dt == "bf16" and plan != "invariant" and rng.random() < 0.5
+    pool = str(rng.choice(["exact", "oversized2x"]))
+    return dict(d=d, bs=bs, dt=dt, hkv=hkv, g=g, nq=nq, lens=[int(x) for x in lens], w=window,
+                plan=plan, tokens=tokens, fused=fused, pool=pool)
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_configuration(gpu, i):
+    c = _draw(i)
+    label = str(c)
+    spec = small_spec(num_seqs=len(c["lens"]), num_q_heads=c["hkv"] * c["g"],
+                      num_kv_heads=c["hkv"], head_dim=c["d"], block_size=c["bs"],
+                      kv_dtype=c["dt"], context=max(c["lens"] + [1]), append=c["fused"],
+                      pool=c["pool"], case_id=9000 + i)
+    if c["nq"] > 1:
+        case = make_multi_query_case(spec, c["nq"], seed=i, context_lens=c["lens"],
+                                     append=c["fused"])
+    else:
+        case = make_case(spec, seed=i, context_lens=c["lens"])
+    ref, ref_lse = _ref(case, c["w"])
+    dev = to_device(case)
+    try:
+        if c["plan"] == "override":
+            gpu.set_split_tokens(c["tokens"])
+        if c["plan"] == "invariant":
+            # the flag is a field of the shape; the binding passes it per call
+            out, lse = _run_invariant(gpu, case, dev, c["w"])
+        else:
+            out, lse = _run(gpu, case, dev, c["w"], fused=c["fused"])
+    finally:
+        gpu.set_split_tokens(0)
+    assert_parity(out, lse, ref, ref_lse, label)
+    if c["fused"]:
+        k = dev["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(k, case["k_pool_full"]), label
+
+
+def _run_invariant(gqa, case, dev, w):
+    max_ctx = int(case["context_lens"].max())
+    args = dict(softmax_scale=case["softmax_scale"], sliding_window=w, batch_invariant=True,
+                k_scale=dev["k_scale"], v_scale=dev["v_scale"])
+    if case.get("num_queries"):
+        out, lse = gqa.paged_decode_multi_query(dev["q"], dev["k_cache"], dev["v_cache"],
+                                                dev["block_tables"], dev["context_lens"],
+                                                max_ctx, **args)
+    else:
+        out, lse = gqa.paged_decode_attention(dev["q"], dev["k_cache"], dev["v_cache"],
+                                              dev["block_tables"], dev["context_lens"],
+                                              max_ctx, **args)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
