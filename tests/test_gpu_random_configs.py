@@ -86,3 +86,72 @@ def _run_invariant(gqa, case, dev, w):
                                               max_ctx, **args)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _draw_fp8_append(i):
+    rng = np.random.default_rng([2024, 13, i])
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    nq = min(int(rng.choice([1, 1, 2, 4])), 32 // g)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    lens = [int(x) for x in rng.integers(1, 3000, int(rng.integers(1, 5)))]
+    plan = str(rng.choice(["default", "invariant", "override"]))
+    tokens = int(rng.choice([128, 512, 2080]))
+    window = 0 if rng.random() < 0.7 else int(rng.integers(8, 1000))
+    return dict(hkv=hkv, g=g, nq=nq, d=d, bs=bs, lens=lens, plan=plan, tokens=tokens, w=window)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_fused_fp8_append(gpu, i):
+    """Fused steps that quantise the new tokens into an fp8 cache (power-of-two
+    block scales, grown and re-encoded as blocks fill) and attend, over random
+    shapes, query positions, windows and split plans: codes and scales bit-exact
+    against the oracle's append after every step, attention within the parity bar."""
+    from tests.test_gpu_fp8_append import (_assert_same, _bf16_dev, _f32_dev, _fp8_case_with_room,
+                                           _i32_dev, _rows, _u8_dev)
+    import oracle
+    c = _draw_fp8_append(i)
+    label = str(c)
+    hq, hkv, d, bs, nq = c["hkv"] * c["g"], c["hkv"], c["d"], c["bs"], c["nq"]
+    steps = 3
+    state, grown = _fp8_case_with_room(hq, hkv, d, bs, c["lens"], steps * nq, 9800 + i, seed=i)
+    dev = [_u8_dev(state[0]), _u8_dev(state[1]), _f32_dev(state[2]), _f32_dev(state[3])]
+    td = _i32_dev(grown)
+    rng = np.random.default_rng([7, i])
+    B = len(c["lens"])
+    ctx = np.array(c["lens"], dtype=np.int32)
+    kw = dict(k_scale=dev[2], v_scale=dev[3], batch_invariant=c["plan"] == "invariant",
+              sliding_window=c["w"])
+    try:
+        if c["plan"] == "override":
+            gpu.set_split_tokens(c["tokens"])
+        for step in range(steps):
+            mags = 2.0 ** rng.uniform(-2, 3, (B, nq, hkv, 1))
+            k_new, v_new = _rows(rng, (B, nq, hkv, d), mags), _rows(rng, (B, nq, hkv, d), mags)
+            q = _rows(rng, (B, nq, hq, d), 1.0)
+            state = oracle.kv_append_fp8(*state, k_new, v_new, grown, ctx, bs)
+            pos = ctx.copy()
+            ctx = ctx + nq
+            if nq == 1:
+                out, lse = gpu.paged_decode_append_attention(
+                    _bf16_dev(q[:, 0]), _bf16_dev(k_new[:, 0]), _bf16_dev(v_new[:, 0]),
+                    _i32_dev(pos), dev[0], dev[1], td, _i32_dev(ctx), int(ctx.max()), d ** -0.5,
+                    **kw)
+                ref, ref_lse = oracle.paged_decode_attention(
+                    q[:, 0], state[0], state[1], grown, ctx, bs, d ** -0.5, "fp8", state[2],
+                    state[3], sliding_window=c["w"])
+            else:
+                out, lse = gpu.paged_decode_multi_query_append(
+                    _bf16_dev(q), _bf16_dev(k_new), _bf16_dev(v_new), dev[0], dev[1], td,
+                    _i32_dev(ctx), int(ctx.max()), d ** -0.5, **kw)
+                ref, ref_lse = oracle.paged_multi_query_attention(
+                    q, state[0], state[1], grown, ctx, bs, d ** -0.5, "fp8", state[2], state[3],
+                    sliding_window=c["w"])
+            torch.cuda.synchronize()
+            _assert_same(tuple(t.cpu().numpy() for t in dev), state, f"{label} step {step}")
+            assert_parity(out.cpu().numpy().astype(np.float64),
+                          lse.cpu().numpy().astype(np.float64), ref, ref_lse,
+                          f"{label} step {step}")
+    finally:
+        gpu.set_split_tokens(0)
