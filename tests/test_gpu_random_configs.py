@@ -155,3 +155,62 @@ def test_random_fused_fp8_append(gpu, i):
                           f"{label} step {step}")
     finally:
         gpu.set_split_tokens(0)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_fused_kivi_append(gpu, i):
+    """The same on KIVI pools (keys scaled per channel, values per token; at most 8
+    rows per KV head): fused quantising steps over random shapes, query positions,
+    windows and split plans, bit-exact codes and scales, attention within the bar."""
+    from tests.test_gpu_kivi import _kivi_room, _rows, _same, _t
+    import oracle
+    rng = np.random.default_rng([2024, 14, i])
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    nq = min(int(rng.choice([1, 1, 2, 4])), 8 // g)
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    lens = [int(x) for x in rng.integers(1, 2500, int(rng.integers(1, 5)))]
+    plan = str(rng.choice(["default", "invariant", "override"]))
+    window = 0 if rng.random() < 0.7 else int(rng.integers(8, 1000))
+    label = str(dict(hkv=hkv, g=g, nq=nq, d=d, bs=bs, lens=lens, plan=plan, w=window))
+    hq = hkv * g
+    steps = 3
+    state, grown = _kivi_room(hq, hkv, d, bs, lens, steps * nq, 9900 + i)
+    dev = [_t(x) for x in state]
+    td = _t(grown)
+    B = len(lens)
+    ctx = np.array(lens, dtype=np.int32)
+    kw = dict(k_scale=dev[2], v_scale=dev[3], batch_invariant=plan == "invariant",
+              sliding_window=window)
+    try:
+        if plan == "override":
+            gpu.set_split_tokens(256)
+        for step in range(steps):
+            mags = 2.0 ** rng.uniform(-2, 3, (B, nq, hkv, d))
+            k_new, v_new = _rows(rng, (B, nq, hkv, d), mags), _rows(rng, (B, nq, hkv, d), mags)
+            q = _rows(rng, (B, nq, hq, d), 1.0)
+            state = oracle.kv_append_fp8(*state, k_new, v_new, grown, ctx, bs, layout="kivi")
+            start = ctx.copy()
+            ctx = ctx + nq
+            if nq == 1:
+                out, lse = gpu.paged_decode_append_attention(
+                    _t(q[:, 0]), _t(k_new[:, 0]), _t(v_new[:, 0]), _t(start), dev[0], dev[1], td,
+                    _t(ctx), int(ctx.max()), d ** -0.5, **kw)
+                ref, ref_lse = oracle.paged_decode_attention(
+                    q[:, 0], state[0], state[1], grown, ctx, bs, d ** -0.5, "fp8_kivi", state[2],
+                    state[3], sliding_window=window)
+            else:
+                out, lse = gpu.paged_decode_multi_query_append(
+                    _t(q), _t(k_new), _t(v_new), dev[0], dev[1], td, _t(ctx), int(ctx.max()),
+                    d ** -0.5, **kw)
+                ref, ref_lse = oracle.paged_multi_query_attention(
+                    q, state[0], state[1], grown, ctx, bs, d ** -0.5, "fp8_kivi", state[2],
+                    state[3], sliding_window=window)
+            torch.cuda.synchronize()
+            _same(tuple(x.cpu().numpy() for x in dev), state, f"{label} step {step}")
+            assert_parity(out.cpu().numpy().astype(np.float64),
+                          lse.cpu().numpy().astype(np.float64), ref, ref_lse,
+                          f"{label} step {step}")
+    finally:
+        gpu.set_split_tokens(0)
