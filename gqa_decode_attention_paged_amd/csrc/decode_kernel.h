@@ -1498,32 +1498,47 @@ __global__ __launch_bounds__(WAVES * kWave, M > 16 ? 1 : 8 / WAVES) void paged_d
 // itself.  The weights are the log-sum-exp merge of the splits' base-2 lse; lane
 // s loads split s's lse, and the float4 columns of the row are shared out over
 // LG lane groups, each taking every LG-th split, so all loads fly together.
+// They are issued with the split count's own load, for the splits below
+// split_cap (the launch's splits per sequence, the most any sequence has unless
+// the slots were shared out by length), so one memory round trip brings them
+// all; slots at or past the count hold stale values, which are masked out.
 // Merges splits in the order s = 0, 1, ... within a lane group, then adds the
 // groups' sums.
 template <int D>
 __global__ __launch_bounds__(kWave) void merge_splits_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     const uint32_t* __restrict__ counters, int32_t num_kv_heads, int32_t M, int32_t max_splits,
-    int32_t Q, int32_t num_q_heads, int32_t G, int32_t group_shift, float* __restrict__ out,
-    float* __restrict__ out_lse) {
+    int32_t split_cap, int32_t Q, int32_t num_q_heads, int32_t G, int32_t group_shift,
+    float* __restrict__ out, float* __restrict__ out_lse) {
   constexpr int C4 = D / 4;                        // float4 columns of a row
   constexpr int LG = kWave / C4;                   // lane groups
   constexpr int PER = kMaxSplits / LG;             // splits per lane group, at most
   const int g = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const size_t pair = (size_t)b * num_kv_heads + kvh;
-  const int nsplit = (int)counters[pair * kCounterStride + kSplitCountWord];
-  if (nsplit < 2) return;
   const size_t prow = pair * max_splits;
   const int col = lane % C4, grp = lane / C4;
-  const float x = lane < nsplit ? ws_lse[(prow + lane) * M + g] : kNegInf;
+  const int nsplit = (int)counters[pair * kCounterStride + kSplitCountWord];
+  const int cap = split_cap < max_splits ? split_cap : max_splits;
+  float x = lane < cap ? ws_lse[(prow + lane) * M + g] : kNegInf;
   f32x4 v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int si = grp + u * LG;
-    v[u] = si < nsplit ? *reinterpret_cast<const f32x4*>(ws_o + ((prow + si) * M + g) * D + 4 * col)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[u] = si < cap ? *reinterpret_cast<const f32x4*>(ws_o + ((prow + si) * M + g) * D + 4 * col)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  if (nsplit < 2) return;
+  if (nsplit > cap) {                              // slots shared out by length: the rest
+    if (lane >= cap && lane < nsplit) x = ws_lse[(prow + lane) * M + g];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int si = grp + u * LG;
+      if (si >= cap && si < nsplit)
+        v[u] = *reinterpret_cast<const f32x4*>(ws_o + ((prow + si) * M + g) * D + 4 * col);
+    }
+  }
+  if (lane >= nsplit) x = kNegInf;
   const bool nan = __any(x != x);
   float mx = x;
 #pragma unroll

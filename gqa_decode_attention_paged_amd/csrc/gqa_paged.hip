@@ -600,10 +600,11 @@ static gqa_status decode_impl(const gqa_paged_shape* s, int32_t num_queries, con
     const float* ml = p.ws_lse;
     const uint32_t* mc = p.counters;
     int32_t hkv = s->num_kv_heads, mcap = row_capacity(rows), msplits = ws_splits, nq = num_queries;
+    int32_t scap = launch_splits;                  // splits loaded with the count
     int32_t hq = s->num_q_heads, g = G, gshift = p.group_shift;
     float* mout = out;
     float* mlse = out_lse;
-    void* margs[] = {&mo, &ml, &mc, &hkv, &mcap, &msplits, &nq, &hq, &g, &gshift, &mout, &mlse};
+    void* margs[] = {&mo, &ml, &mc, &hkv, &mcap, &msplits, &scap, &nq, &hq, &g, &gshift, &mout, &mlse};
     const void* mfn = s->head_dim == 64 ? reinterpret_cast<const void*>(&gqa::merge_splits_kernel<64>)
                                         : reinterpret_cast<const void*>(&gqa::merge_splits_kernel<128>);
     const hipError_t me = hipLaunchKernel(mfn, dim3(rows, s->num_kv_heads, s->num_seqs), dim3(64),

@@ -81,6 +81,23 @@ def test_multi_query_ragged_on_four_wave_workgroups(gpu, hq, nq, dt):
     assert_parity(out, lse, ref, ref_lse, f"24 ragged sequences, G={hq // 8} Q={nq} {dt}")
 
 
+@pytest.mark.parametrize("nq,dt", [(4, "bf16"), (2, "fp8")])
+def test_one_long_sequence_among_short_ones_merged_in_second_launch(gpu, nq, dt):
+    """16 or more rows merge in a launch of their own, which loads the splits
+    below the launch's per-sequence split count S together with the count.  The
+    length-proportional sharing gives the long sequence about 0.87 of the 8 S
+    slots of each KV head (capped at 7000 / 128 splits), far more than S, so the
+    merge also loads the rest."""
+    lens = [7000] + [nq + 37 * i for i in range(1, 8)]
+    spec = small_spec(num_seqs=8, num_q_heads=32 if dt == "bf16" else 64, num_kv_heads=8,
+                      head_dim=128, block_size=16, kv_dtype=dt, context=7000,
+                      case_id=6750 + nq)
+    case = make_multi_query_case(spec, nq, seed=9, context_lens=lens, append=(dt == "bf16"))
+    ref, ref_lse = _reference(case)
+    out, lse = _verify_step(gpu, case, to_device(case))
+    assert_parity(out, lse, ref, ref_lse, f"one long sequence, Q={nq} {dt}")
+
+
 @pytest.mark.parametrize("batch_invariant", [False, True])
 @pytest.mark.parametrize("hq,hkv,nq,dt", [(32, 8, 2, "bf16"), (32, 8, 4, "bf16"),
                                           (8, 4, 2, "fp8"), (8, 4, 4, "fp8")])
