@@ -382,7 +382,7 @@ def main():
                     help="split every sequence by its own length only (GQA_FLAG_BATCH_INVARIANT)")
     ap.add_argument("--split-tokens", type=int, default=0, metavar="T",
                     help="split-length override (gqa_set_split_tokens): the batch-invariant "
-                         "plan with splits of at least T tokens")
+                         "plan with about one split per T tokens")
     ap.add_argument("--no-sustained", action="store_true",
                     help="skip the read probe of the workload's tile pattern")
     ap.add_argument("--probe", action="store_true",
@@ -565,7 +565,7 @@ def main():
             "block_table": "identity (control run)" if args.identity_table else "random permutation",
             "kv_bytes_per_step": kv_bytes, "pool_copies_rotated": copies,
             "reuse_distance_bytes": (min(copies, args.steps) - 1) * kv_bytes,
-            "split_policy": (f"batch-invariant, splits of at least {args.split_tokens} tokens"
+            "split_policy": (f"batch-invariant, about one split per {args.split_tokens} tokens"
                              if args.split_tokens else
                              "batch-invariant" if inv else "default (fills the GPU once)"),
         },

@@ -258,7 +258,7 @@ def num_splits(context_len: int) -> int:
 def set_split_tokens(tokens: int) -> None:
     """Set (a multiple of 32 in [128, 2^19]) or clear (0) the process-wide
     split-length override; while set, attention calls split each sequence by its
-    own length with splits of at least that many tokens."""
+    own length into about one split per that many tokens (at most 64 splits)."""
     _check(load().gqa_set_split_tokens(int(tokens)))
 
 

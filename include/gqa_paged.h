@@ -74,7 +74,7 @@
  *  - Split-length override: GQA_SPLIT_TOKENS (read once per process, or set at
  *    run time with gqa_set_split_tokens) = T, a multiple of 32 in [128, 2^19].
  *    When set, every attention call splits each sequence by its own length
- *    with splits of at least T tokens (at most 64 of them), as under
+ *    into about one split per T tokens (at most 64; gqa_decode_num_splits), as under
  *    GQA_FLAG_BATCH_INVARIANT with T in place of 128: results stay
  *    batch-invariant, and T trades that mode's split count for its cost.
  */
