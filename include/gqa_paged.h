@@ -249,14 +249,17 @@ size_t gqa_paged_decode_workspace_size(const gqa_paged_shape* shape, int32_t max
  *                 the status word.  The first B*H_kv*64 words
  *                 (B*H_kv*256 bytes) must be zero before the first
  *                 call (gqa_paged_decode_workspace_init, or any zero fill); every
- *                 call leaves the counters zero again, so a workspace prepared once
+ *                 call leaves each arrival counter (the first word of its 256
+ *                 bytes) zero again, so a workspace prepared once
  *                 serves any later call with no more (sequence, KV head) pairs (the
  *                 status word keeps its bits until cleared).  One
  *                 workspace serves one call at a time: calls sharing it must be
  *                 ordered on one stream.
  * Inputs are read only.  One kernel runs on `stream`: each workgroup attends
  * over one context split of one (sequence, KV head); the last workgroup of a
- * (sequence, KV head) to finish merges the splits by log-sum-exp.
+ * (sequence, KV head) to finish merges the splits by log-sum-exp.  With 16 or
+ * more query rows per KV head (or GQA_DEFER_MERGE=1) the splits merge in a
+ * second kernel on the same stream instead.
  */
 gqa_status gqa_paged_decode_attention(const gqa_paged_shape* shape,
                                       const void* q,
