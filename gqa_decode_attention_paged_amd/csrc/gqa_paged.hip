@@ -57,8 +57,10 @@ gqa_status check_shape(const gqa_paged_shape* s) {
   if (s->head_dim < 1 || s->block_size < 1)
     return fail(GQA_ERR_INVALID_ARG, "head_dim and block_size must be >= 1");
   const int G = s->num_q_heads / s->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(GQA_ERR_UNSUPPORTED, "group size G=%d not in {1,2,4,8}", G);
+  // A KV head's rows (G per query position) map to heads by shift and mask, and
+  // the kernels take at most 32 of them (checked per call, with the positions).
+  if (G > 32 || (G & (G - 1)) != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "group size G=%d not in {1,2,4,8,16,32}", G);
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(GQA_ERR_UNSUPPORTED, "head_dim=%d not in {64,128}", s->head_dim);
   if (s->block_size != 16 && s->block_size != 32)

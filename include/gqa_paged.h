@@ -50,7 +50,8 @@
  *    are never read.
  *  - Supported shapes: head_dim in {64, 128}; block_size in {16, 32};
  *    num_q_heads % num_kv_heads == 0 with G = num_q_heads / num_kv_heads in
- *    {1, 2, 4, 8}; kv_dtype BF16 or FP8_E4M3.  Anything else returns
+ *    {1, 2, 4, 8, 16, 32}, and G * (query positions) <= 32 rows per KV head
+ *    (<= 8 for KIVI pools); kv_dtype BF16 or FP8_E4M3.  Anything else returns
  *    GQA_ERR_UNSUPPORTED.  Device pointers must be 16-byte aligned.
  *  - Errors: a call validates its host-side arguments and returns a status; it
  *    never aborts.  gqa_last_error() gives a message for the last non-OK status

@@ -116,6 +116,7 @@ def _call_decode(lib, shape, ws_bytes=1 << 30, ptr=16, **over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(head_dim=96), 2), (dict(block_size=8), 2), (dict(num_q_heads=24), 2),
+    (dict(num_q_heads=512), 2), (dict(num_q_heads=96), 2),   # G = 64; G = 12
     (dict(num_q_heads=30), 1), (dict(num_seqs=-1), 1), (dict(kv_dtype=7), 2),
     (dict(num_blocks=0), 1), (dict(flags=6), 1),
 ])
@@ -139,6 +140,13 @@ def test_fp8_needs_scales(lib):
 
 def test_zero_sequences_return_ok_without_launching(lib):
     assert _call_decode(lib, _shape(num_seqs=0)) == 0
+
+
+@pytest.mark.parametrize("hq,status", [(128, 0), (256, 0), (512, 2)])
+def test_group_sizes_up_to_32_are_accepted(lib, hq, status):
+    """G = 16 and 32 (8 KV heads) pass the shape checks; G = 64 is more rows than
+    a kernel takes.  No sequences, so nothing launches."""
+    assert _call_decode(lib, _shape(num_seqs=0, num_q_heads=hq)) == status
 
 
 def test_fused_append_validation(lib):

@@ -53,6 +53,8 @@ def _verify_step(gqa, case, dev, max_context_len=None, batch_invariant=False):
     (64, 8, 4, 128, 32, "fp8"),      # fp8, G=8, 4 positions: 32 rows (matrix path)
     (32, 8, 4, 128, 16, "fp8"),      # fp8, 16 rows
     (16, 8, 3, 64, 16, "fp8"),       # fp8, 6 rows, d=64
+    (128, 8, 2, 128, 16, "bf16"),    # G=16, 2 positions: 32 rows
+    (32, 1, 1, 64, 32, "fp8"),       # G=32 (multi-query attention), one position
 ])
 def test_multi_query_parity(gpu, hq, hkv, nq, d, bs, dt):
     lens = [nq, nq + 1, 100, 1000, 3000]

@@ -300,3 +300,23 @@ def test_unused_block_scales_are_never_used(gpu, hq, hkv, dt):
     ref, ref_lse = run_oracle(case)
     out, lse = run_step(gpu, to_device(case), case)
     assert_parity(out, lse, ref, ref_lse, f"NaN scales in unused block 0, G={hq // hkv} {dt}")
+
+
+@pytest.mark.parametrize("hq,hkv,dt", [(128, 8, "bf16"), (32, 1, "bf16"), (64, 4, "fp8"),
+                                       (32, 1, "fp8")])
+def test_sixteen_or_more_query_heads_per_kv_head(gpu, hq, hkv, dt):
+    """One position with G = 16 or 32 (multi-query attention at G = 32): 16 or more
+    rows per KV head, so K is staged through LDS and the splits merge in a launch
+    of their own.  Ragged lengths with an empty sequence; bf16 also through the
+    fused append-and-attend entry point."""
+    lens = [2500, 37, 0, 1200, 640]
+    spec = small_spec(num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                      block_size=16, kv_dtype=dt, context=2500, append=(dt == "bf16"),
+                      case_id=5300 + hq + hkv + (dt == "fp8"))
+    case = make_case(spec, seed=2, context_lens=lens)
+    ref, ref_lse = run_oracle(case)
+    out, lse = run_step(gpu, to_device(case), case)
+    assert_parity(out, lse, ref, ref_lse, f"G={hq // hkv} {dt}")
+    if dt == "bf16":
+        out, lse = run_fused_step(gpu, to_device(case), case)
+        assert_parity(out, lse, ref, ref_lse, f"fused, G={hq // hkv}")
